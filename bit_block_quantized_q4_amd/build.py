@@ -1,0 +1,86 @@
+"""Build libq4.so for gfx950 in-tree.
+
+Usage: ``python -m bit_block_quantized_q4_amd.build`` (or ``build()``).
+Every HIP translation unit is compiled with hipcc for ``--offload-arch=gfx950``
+in parallel, then linked into ``bit_block_quantized_q4_amd/libq4.so``.  The
+build always recompiles; the library is written atomically.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+INCLUDE = ROOT / "include"
+BUILD_DIR = PKG / "_build"
+LIB_PATH = PKG / "libq4.so"
+ARCH = os.environ.get("Q4_OFFLOAD_ARCH", "gfx950")
+
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+    # Disable packed fp32 instructions in device code (v_pk_*_f32).
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}",
+    f"-I{CSRC}",
+]
+
+
+def _hipcc() -> str:
+    cand = os.environ.get("HIPCC")
+    if cand:
+        return cand
+    for p in ("/opt/rocm/bin/hipcc",):
+        if os.path.exists(p):
+            return p
+    return "hipcc"
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass warns that it does not know the device-only feature.
+    out = "\n".join(
+        ln for ln in res.stdout.splitlines()
+        if "packed-fp32-ops' is not a recognized feature" not in ln)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{out}")
+    if out.strip() and verbose:
+        print(out, flush=True)
+
+
+def build(verbose: bool = False) -> Path:
+    """Compile every csrc/*.hip for gfx950 and link libq4.so; returns its path."""
+    hipcc = _hipcc()
+    BUILD_DIR.mkdir(exist_ok=True)
+    srcs = sorted(CSRC.glob("*.hip"))
+    if not srcs:
+        raise RuntimeError(f"no HIP sources under {CSRC}")
+    objs = [BUILD_DIR / (s.stem + ".o") for s in srcs]
+    jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = [ex.submit(_run, [hipcc, *COMMON_FLAGS, "-c", str(s), "-o", str(o)], verbose)
+                for s, o in zip(srcs, objs)]
+        for f in futs:
+            f.result()
+    tmp = LIB_PATH.with_suffix(".so.tmp")
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp),
+          *map(str, objs)], verbose)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    p = build(verbose="-v" in sys.argv)
+    print(p)

@@ -1,0 +1,118 @@
+// libq4 C ABI: argument validation and dispatch.  Every check runs on the host
+// before anything touches the device; the library keeps no state, never
+// allocates, frees or synchronises.
+#include "q4.h"
+#include "q4_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kMaxRows = int64_t(1) << 31;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int dt) { return dt == Q4_F32 || dt == Q4_F16; }
+
+size_t dtype_bytes(int dt) { return dt == Q4_F32 ? 4 : 2; }
+
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a);
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+bool valid_nk(int64_t n, int64_t k) {
+  return n >= 1 && k >= Q4_QK && k % Q4_QK == 0 && n < kMaxRows &&
+         k < kMaxElems && n <= kMaxElems / k;
+}
+
+q4_status from_hip(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_HIP; }
+
+q4_status check_matmul(const void* x, int x_dtype, const void* packed, void* y,
+                       int y_dtype, int64_t m, int64_t n, int64_t k) {
+  if (!x || !packed || !y) return Q4_ERR_INVALID_ARG;
+  if (!valid_nk(n, k) || m < 1 || m >= kMaxRows || m > kMaxElems / k ||
+      m > kMaxElems / n)
+    return Q4_ERR_SHAPE;
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return Q4_ERR_DTYPE;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(y)) return Q4_ERR_ALIGNMENT;
+  const size_t ybytes = static_cast<size_t>(m) * n * dtype_bytes(y_dtype);
+  const size_t xbytes = static_cast<size_t>(m) * k * dtype_bytes(x_dtype);
+  if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, packed, q4_packed_size(n, k)))
+    return Q4_ERR_INVALID_ARG;
+  return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4_abi_version(void) { return Q4_ABI_VERSION; }
+
+const char* q4_status_string(int status) {
+  switch (status) {
+    case Q4_OK: return "ok";
+    case Q4_ERR_INVALID_ARG: return "invalid argument (null pointer or overlapping buffers)";
+    case Q4_ERR_SHAPE: return "invalid shape (need m, n >= 1, k >= 32, k % 32 == 0, within size limits)";
+    case Q4_ERR_DTYPE: return "unsupported dtype for this call";
+    case Q4_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case Q4_ERR_HIP: return "HIP runtime refused the kernel launch";
+    case Q4_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown q4 status";
+  }
+}
+
+size_t q4_packed_size(int64_t n, int64_t k) {
+  if (!valid_nk(n, k)) return 0;
+  return static_cast<size_t>(n) * static_cast<size_t>(k / Q4_QK) * Q4_BLOCK_BYTES;
+}
+
+q4_status q4_quantize(const void* w, int w_dtype, int64_t n, int64_t k, void* packed,
+                      q4_stream_t stream) {
+  if (!w || !packed) return Q4_ERR_INVALID_ARG;
+  if (!valid_nk(n, k)) return Q4_ERR_SHAPE;
+  if (!valid_dtype(w_dtype)) return Q4_ERR_DTYPE;
+  if (!aligned16(w) || !aligned16(packed)) return Q4_ERR_ALIGNMENT;
+  if (overlap(w, static_cast<size_t>(n) * k * dtype_bytes(w_dtype), packed,
+              q4_packed_size(n, k)))
+    return Q4_ERR_INVALID_ARG;
+  return from_hip(q4::launch_quantize(w, static_cast<q4::DType>(w_dtype), n, k,
+                                      static_cast<uint8_t*>(packed),
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+q4_status q4_gemv(const void* x, int x_dtype, const void* packed, void* y, int y_dtype,
+                  int64_t m, int64_t n, int64_t k, q4_stream_t stream) {
+  const q4_status st = check_matmul(x, x_dtype, packed, y, y_dtype, m, n, k);
+  if (st != Q4_OK) return st;
+  if (m > Q4_GEMV_MAX_M) return Q4_ERR_SHAPE;
+  return from_hip(q4::launch_gemv(x, static_cast<q4::DType>(x_dtype),
+                                  static_cast<const uint8_t*>(packed), y,
+                                  static_cast<q4::DType>(y_dtype), static_cast<int>(m),
+                                  n, k, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t q4_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
+  if (!valid_nk(n, k) || m < 1 || m >= kMaxRows) return 0;
+  return q4::gemm_workspace_bytes(m, n, k);
+}
+
+q4_status q4_gemm(const void* x, int x_dtype, const void* packed, void* y, int y_dtype,
+                  int64_t m, int64_t n, int64_t k, void* workspace,
+                  size_t workspace_bytes, q4_stream_t stream) {
+  const q4_status st = check_matmul(x, x_dtype, packed, y, y_dtype, m, n, k);
+  if (st != Q4_OK) return st;
+  if (x_dtype != Q4_F16) return Q4_ERR_DTYPE;
+  const size_t need = q4::gemm_workspace_bytes(m, n, k);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return Q4_ERR_ALIGNMENT;
+  }
+  return from_hip(q4::launch_gemm(x, q4::DType::F16, static_cast<const uint8_t*>(packed),
+                                  y, static_cast<q4::DType>(y_dtype), m, n, k,
+                                  need > 0 ? workspace : nullptr,
+                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

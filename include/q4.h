@@ -1,0 +1,136 @@
+/*
+ * libq4 -- Q4_0 block-quantised linear layers on AMD Instinct MI355X (gfx950).
+ *
+ * The C ABI of the library.  Plain pointers and sizes only; no HIP or torch
+ * types appear in a signature (a stream is passed as an opaque pointer that
+ * is a hipStream_t).
+ *
+ * The operation
+ * -------------
+ * "Vertical disaggregation: maximizing throughput on heterogeneous silicon",
+ * section "Every cycle counts: custom kernels": the CPU and GPU backends share
+ * one Q4_0 weight copy, output is deterministic, and the kernel stages are
+ * nibble unpack, dot product, scale application, batched decode and a GPU
+ * path onto matrix cores for prefill.  The format itself is not printed on
+ * the page; this library fixes it as:
+ *
+ *   - a weight W[n][k] (row-major, n output features, k input features) is
+ *     split along k into blocks of 32 (k must be a multiple of 32);
+ *   - each block is 18 bytes: a 2-byte little-endian IEEE fp16 scale d, then
+ *     16 code bytes; byte i holds the 4-bit code q of element i in its low
+ *     nibble and of element i+16 in its high nibble;
+ *   - a weight decodes as w = (q - 8) * d;
+ *   - the packed buffer is n rows of k/32 consecutive blocks, rows
+ *     contiguous: n * (k/32) * 18 bytes, no padding.
+ *
+ * Quantiser: m is the block element of largest magnitude (the first on a
+ * tie); d = fp16(m / -8) rounded to nearest even, subnormals kept;
+ * q = min(15, trunc(x / d + 8.5)) with x / d a correctly rounded fp32 division
+ * by the fp16 scale widened to fp32 and the + 8.5 an fp32 addition; every q is
+ * 8 when d is zero.
+ *
+ * Matmul: y[m][n] = sum_k x[m][k] * w[n][k] (x row-major [m][k], y row-major
+ * [m][n]), accumulated in fp32.  Results are deterministic: identical inputs,
+ * shapes and dtypes on the same device and build give identical bits (no
+ * atomics, fixed reduction order).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *   - all data pointers are device pointers owned by the caller; the library
+ *     never allocates, frees or synchronises, keeps no state, and is safe to
+ *     call from several host threads;
+ *   - every call is asynchronous on `stream` (NULL = the null stream); errors
+ *     detected on the host return before anything is launched; a failed
+ *     launch returns Q4_ERR_HIP; faults during execution surface at the
+ *     caller's next synchronisation, as for any HIP library;
+ *   - every data pointer must be 16-byte aligned (Q4_ERR_ALIGNMENT) and
+ *     non-NULL (Q4_ERR_INVALID_ARG); outputs must not overlap inputs
+ *     (Q4_ERR_INVALID_ARG);
+ *   - shapes: n >= 1, m >= 1, k >= 32 and k % 32 == 0, and n * k below 2^40
+ *     (Q4_ERR_SHAPE);
+ *   - inputs must be finite; weights must satisfy |w| < 65520 * 8 so that d
+ *     is finite.  This is not checked on the device.
+ */
+#ifndef LIBQ4_Q4_H
+#define LIBQ4_Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_ABI_VERSION 1
+#define Q4_QK 32            /* weights per block */
+#define Q4_BLOCK_BYTES 18   /* bytes per block */
+#define Q4_GEMV_MAX_M 32    /* largest batch accepted by q4_gemv */
+
+/* An opaque hipStream_t. */
+typedef struct ihipStream_t *q4_stream_t;
+
+typedef enum q4_status {
+  Q4_OK = 0,
+  Q4_ERR_INVALID_ARG = 1, /* NULL pointer, overlapping buffers */
+  Q4_ERR_SHAPE = 2,       /* m, n or k out of range, k % 32 != 0 */
+  Q4_ERR_DTYPE = 3,       /* dtype code not supported by this call */
+  Q4_ERR_ALIGNMENT = 4,   /* a pointer is not 16-byte aligned */
+  Q4_ERR_HIP = 5,         /* the HIP runtime refused a launch */
+  Q4_ERR_WORKSPACE = 6    /* workspace missing or smaller than required */
+} q4_status;
+
+typedef enum q4_dtype {
+  Q4_F32 = 0, /* IEEE binary32 */
+  Q4_F16 = 1  /* IEEE binary16 */
+} q4_dtype;
+
+/* Version of this ABI (Q4_ABI_VERSION). */
+int q4_abi_version(void);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char *q4_status_string(int status);
+
+/* Size in bytes of a packed [n][k] Q4_0 weight: n * (k/32) * 18.
+ * Returns 0 when the shape is invalid (n < 1, k < 32, k % 32 != 0). */
+size_t q4_packed_size(int64_t n, int64_t k);
+
+/* Quantise a row-major [n][k] weight `w` of dtype `w_dtype` (Q4_F32 or
+ * Q4_F16; fp16 is widened exactly to fp32 first) into `packed`, which must
+ * hold q4_packed_size(n, k) bytes.  The result is bit-identical to the rule
+ * stated at the top of this header.  Reads 4 (fp32) or 2 (fp16) bytes and
+ * writes 0.5625 bytes per weight. */
+q4_status q4_quantize(const void *w, int w_dtype, int64_t n, int64_t k,
+                      void *packed, q4_stream_t stream);
+
+/* Batched-decode GEMV: y[m][n] = x[m][k] . dequant(packed)^T for
+ * 1 <= m <= Q4_GEMV_MAX_M (the "batch decode" stage).  x is Q4_F32 or
+ * Q4_F16, y is Q4_F32 or Q4_F16.  Every output is the fp32 sum over blocks of
+ * d times the exact block dot product of x with (q - 8), rounded once to the
+ * output dtype.  Streams each packed byte from memory once per call. */
+q4_status q4_gemv(const void *x, int x_dtype, const void *packed, void *y,
+                  int y_dtype, int64_t m, int64_t n, int64_t k,
+                  q4_stream_t stream);
+
+/* Bytes of workspace q4_gemm needs for this shape (0 when none). */
+size_t q4_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
+
+/* Prefill GEMM: y[m][n] = x[m][k] . dequant(packed)^T for any m >= 1 (the
+ * "GPU Q4_0 -> Tensor Core path"): weight tiles are dequantised to fp16
+ * (w = (q - 8) * d rounded once) and contracted on fp16 matrix cores with fp32
+ * accumulation.  Because the weights are rounded to fp16, every block scale
+ * must satisfy |d| <= 8188 (every dequantised weight within the fp16 range,
+ * |w| <= 65504); larger scales give infinite outputs (not checked; q4_gemv has
+ * no such limit).  x must be Q4_F16; y is Q4_F32 or Q4_F16.  `workspace` must
+ * hold q4_gemm_workspace_size(m, n, k) bytes (it may be NULL when that is
+ * 0); its contents on entry are ignored.  A prompt processed in row chunks
+ * passes x + c*rows*k and y + c*rows*n for chunk c. */
+q4_status q4_gemm(const void *x, int x_dtype, const void *packed, void *y,
+                  int y_dtype, int64_t m, int64_t n, int64_t k,
+                  void *workspace, size_t workspace_bytes,
+                  q4_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBQ4_Q4_H */

@@ -141,12 +141,18 @@ def dequantize(packed: np.ndarray, n: int, k: int) -> np.ndarray:
     return (qm8 * D[..., None]).reshape(n, k)
 
 
-def matmul_ref(x: np.ndarray, packed: np.ndarray, n: int, k: int):
+def matmul_ref(x: np.ndarray, packed: np.ndarray, n: int, k: int, cols=None):
     """(y, S) for y = x . dequant(W)^T and S = |x| . |dequant(W)|^T, both fp64.
 
     x is a row-major [m, k] fp16/fp32 activation; every product x*w is exact
     in fp64, so y differs from the exact sum only by fp64 summation error.
+    ``cols`` optionally restricts the output features to those rows of W
+    (y then has len(cols) columns, in that order).
     """
+    if cols is not None:
+        cols = np.asarray(cols)
+        packed = np.asarray(packed).reshape(n, -1)[cols]
+        n = len(cols)
     xa = np.asarray(x)
     if xa.dtype not in (np.float16, np.float32):
         raise TypeError(f"unsupported activation dtype {xa.dtype}")

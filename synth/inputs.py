@@ -113,8 +113,24 @@ def outlier_weights(rng: np.random.Generator, n: int, k: int,
 
 
 def student_t_weights(rng: np.random.Generator, n: int, k: int,
-                      nu: float = 3.0, sigma: float = 0.02) -> np.ndarray:
-    w = rng.standard_t(nu, size=(n, k)).astype(np.float32)
+                      sigma: float = 0.02) -> np.ndarray:
+    """Student-t with 3 degrees of freedom, times sigma.
+
+    Drawn from the definition t = Z / sqrt(V / 3) with V ~ chi-square(3),
+    and V built as chi-square(2) + chi-square(1) = -2 ln U + Z1^2
+    (U uniform on (0, 1], Z, Z1 standard normal, all independent).
+    """
+    w = rng.standard_normal((n, k), dtype=np.float32)
+    v = rng.standard_normal((n, k), dtype=np.float32)
+    np.multiply(v, v, out=v)
+    u = rng.random((n, k), dtype=np.float32)
+    np.subtract(np.float32(1.0), u, out=u)          # (0, 1]
+    np.log(u, out=u)
+    v -= np.float32(2.0) * u
+    del u
+    v *= np.float32(1.0 / 3.0)
+    np.sqrt(v, out=v)
+    w /= v
     w *= np.float32(sigma)
     return w
 
@@ -165,16 +181,16 @@ def random_activations(seed: int, m: int, k: int, dtype: str = "f16") -> np.ndar
     return x
 
 
-def edge_case_weights(seed: int, n: int, k: int) -> np.ndarray:
+def edge_case_weights(seed: int, n: int, k: int, top: float = 5.0e5) -> np.ndarray:
     """Rows of Q4_0 blocks that exercise every corner of the quantiser rule.
 
     Each 32-wide block gets one pattern, cycling through: ordinary N(0,1)
     scaled values; all +0; all -0; +a/-a magnitude ties (first index must
     win); a constant block; values small enough that the fp16 scale is
     subnormal or rounds to zero; values near the top of the fp16 scale
-    range; one huge element among tiny ones; exact multiples of the scale
-    (ties at the rounding boundary); and blocks whose maximum sits at the
-    last index.
+    range (magnitudes up to ``top``); one huge element among tiny ones; exact
+    multiples of the scale (ties at the rounding boundary); and blocks whose
+    maximum sits at the last index.
     """
     rng = rng_for(seed, 0, 3 + n * 19 + k * 23)
     nb = k // QK
@@ -202,8 +218,8 @@ def edge_case_weights(seed: int, n: int, k: int) -> np.ndarray:
             elif p == 6:
                 blk = v * np.float32(1e-9)        # d rounds to (signed) zero
             elif p == 7:
-                blk = v * np.float32(4.0e4)       # d near the top of fp16 range
-                blk = np.clip(blk, -5.0e5, 5.0e5).astype(np.float32)
+                blk = v * np.float32(top / 12.0)  # d near the top of its range
+                blk = np.clip(blk, -top, top).astype(np.float32)
             elif p == 8:
                 blk = v * np.float32(1e-4)
                 blk[rng.integers(QK)] = np.float32(rng.choice([-1, 1]) * 3.0)

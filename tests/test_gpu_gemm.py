@@ -1,0 +1,127 @@
+"""GPU prefill GEMM parity against the oracle: every checked output within
+1e-3 * sum|w*x| + 1e-6; chunked prefill and whole-batch both in tolerance;
+deterministic."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _gpu import assert_matmul_close, sample_rows, to_dev, to_host, workload_weights_cached
+
+pytestmark = pytest.mark.gpu
+
+
+def ytorch(ydt):
+    import torch
+    return torch.float16 if ydt == "f16" else torch.float32
+
+
+def run_gemm(q4, x, packed, n, k, ydt, dev):
+    y = q4.q4_gemm(to_dev(x, dev), to_dev(packed, dev), y_dtype=ytorch(ydt), n=n, k=k)
+    return to_host(y)
+
+
+@pytest.mark.parametrize("m", [1, 33, 128, 200, 257, 640])
+@pytest.mark.parametrize("n,k", [(1, 32), (100, 64), (128, 96), (300, 544), (129, 5120), (520, 2080)])
+def test_shapes(q4lib, gpu, m, n, k):
+    w = synth.random_weights(m + n + k, n, k, "student_t")
+    x = synth.random_activations(m * 5 + k, m, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemm(q4lib, x, packed, n, k, "f16", gpu)
+    assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")
+
+
+@pytest.mark.parametrize("m", [64, 300])
+def test_fp32_output(q4lib, gpu, m):
+    n, k = 200, 1024
+    w = synth.random_weights(8, n, k, "outlier")
+    x = synth.random_activations(9, m, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemm(q4lib, x, packed, n, k, "f32", gpu)
+    assert_matmul_close(g, x, packed, n, k, what=f"f32 out m{m}")
+
+
+def test_one_hot_rows_select_weights(q4lib, gpu):
+    """x = identity: y[i, n] is element i's weight (fp16-rounded), pinning the nibble layout."""
+    n, k = 96, 128
+    w = synth.random_weights(5, n, k, "student_t")
+    packed = oracle.quantize(w)
+    x = np.eye(k, dtype=np.float16)
+    g = run_gemm(q4lib, x, packed, n, k, "f32", gpu)
+    assert_matmul_close(g, x, packed, n, k, what="one-hot")
+
+
+def test_edge_case_weights(q4lib, gpu):
+    """Every quantiser corner case whose dequantised weights fit fp16 (|w| <= 65504)."""
+    n, k = 96, 32 * 24
+    w = synth.edge_case_weights(7, n, k, top=65504.0)
+    x = synth.random_activations(8, 160, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemm(q4lib, x, packed, n, k, "f32", gpu)
+    assert_matmul_close(g, x, packed, n, k, what="edge")
+
+
+def test_prefill_chunked_and_whole(q4lib, gpu):
+    """2048 prompt rows as one batch and as 8 chunks of 256 (pointer offsets)."""
+    import torch
+    wl = synth.WORKLOADS[4]
+    lin = wl.linears[0]
+    w = workload_weights_cached(wl, lin)
+    packed_d = q4lib.q4_quantize(to_dev(w, gpu))
+    packed = to_host(packed_d)
+    del w
+    x = synth.workload_activations(wl, lin.k, 2048)
+    xd = to_dev(x, gpu)
+    whole = q4lib.q4_gemm(xd, packed_d, y_dtype=torch.float16)
+    chunked = torch.empty_like(whole)
+    for c in range(8):
+        q4lib.q4_gemm(xd[c * 256:(c + 1) * 256], packed_d, y=chunked[c * 256:(c + 1) * 256])
+    rows = np.unique(np.concatenate([sample_rows(2048, 40, 1), [255, 256, 1023, 1024, 1792]]))
+    for name, y in (("whole", whole), ("chunked", chunked)):
+        assert_matmul_close(to_host(y)[rows], x[rows], packed, lin.n, lin.k,
+                            what=f"{wl.name}/{name}")
+    again = q4lib.q4_gemm(xd, packed_d, y_dtype=torch.float16)
+    assert torch.equal(again.view(torch.int16), whole.view(torch.int16))
+
+
+def test_layer_workload_sampled(q4lib, gpu):
+    """All seven Student-t linears at M = 256 and 4096, sampled rows x all features."""
+    import torch
+    wl = synth.WORKLOADS[5]
+    for lin in wl.linears:
+        w = workload_weights_cached(wl, lin)
+        packed_d = q4lib.q4_quantize(to_dev(w, gpu))
+        packed = to_host(packed_d)
+        del w
+        for m in (256, 4096):
+            x = synth.workload_activations(wl, lin.k, m)
+            y = to_host(q4lib.q4_gemm(to_dev(x, gpu), packed_d, y_dtype=torch.float16))
+            rows = sample_rows(m, 12, m + lin.tensor_id)
+            assert_matmul_close(y[rows], x[rows], packed, lin.n, lin.k,
+                                what=f"layer/{lin.name} m{m}")
+
+
+def test_deterministic(q4lib, gpu):
+    import torch
+    n, k = 3000, 5120
+    packed = q4lib.q4_quantize(to_dev(synth.random_weights(2, n, k), gpu))
+    x = to_dev(synth.random_activations(3, 700, k, "f16"), gpu)
+    a = q4lib.q4_gemm(x, packed, y_dtype=torch.float32)
+    b = q4lib.q4_gemm(x, packed, y_dtype=torch.float32)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_largest_fp16_scale(q4lib, gpu):
+    """Blocks whose scale is the largest the fp16 dequant path accepts (|d| = 8188)."""
+    n, k = 40, 256
+    w = synth.random_weights(21, n, k) * np.float32(1e5)
+    w = np.clip(w, -65504, 65504).astype(np.float32)
+    w[:, ::32] = np.float32(65504) * np.sign(w[:, ::32] + np.float32(0.5))
+    packed = oracle.quantize(w)
+    d, _ = oracle.unpack(packed, n, k)
+    assert np.abs(d.astype(np.float32)).max() == 8188
+    x = synth.random_activations(22, 70, k, "f16") * np.float16(0.01)
+    g = run_gemm(q4lib, x, packed, n, k, "f32", gpu)
+    assert np.all(np.isfinite(g))
+    assert_matmul_close(g, x, packed, n, k, what="largest scale")

@@ -1,0 +1,136 @@
+"""GPU batched-decode GEMV parity against the oracle: every output within
+1e-3 * sum|w*x| + 1e-6, exact where the arithmetic is exact, deterministic."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _golden import load
+from _gpu import assert_matmul_close, to_dev, to_host, workload_weights_cached
+
+pytestmark = pytest.mark.gpu
+
+BLOCKS, _ = load()
+TDT = {"f16": np.float16, "f32": np.float32}
+
+
+def run_gemv(q4, x, packed, n, k, ydt, dev):
+    import torch
+    ydtype = torch.float16 if ydt == "f16" else torch.float32
+    y = q4.q4_gemv(to_dev(x, dev), to_dev(packed, dev), y_dtype=ydtype, n=n, k=k)
+    return to_host(y)
+
+
+def test_golden_worked_dot(q4lib, gpu):
+    blk = next(b for b in BLOCKS if b.name == "A")
+    packed = oracle.quantize(blk.x[None, :])
+    for xdt in ("f16", "f32"):
+        y = run_gemv(q4lib, np.ones((1, 32), TDT[xdt]), packed, 1, 32, "f32", gpu)
+        assert y[0, 0] == -2.0
+
+
+@pytest.mark.parametrize("xdt", ["f16", "f32"])
+def test_one_hot_rows_give_exact_weights(q4lib, gpu, xdt):
+    """x = identity: y[i, n] = (q - 8) * d of element i, exactly (pins the nibble layout)."""
+    n, k = 70, 64
+    w = synth.random_weights(3, n, k, "student_t")
+    packed = oracle.quantize(w)
+    deq = oracle.dequantize(packed, n, k)
+    for r0 in (0, 32):
+        x = np.zeros((32, k), TDT[xdt])
+        x[np.arange(32), r0 + np.arange(32)] = 1
+        y = run_gemv(q4lib, x, packed, n, k, "f32", gpu)
+        assert np.array_equal(y, deq[:, r0:r0 + 32].T)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 10, 16, 17, 31, 32])
+@pytest.mark.parametrize("n,k", [(1, 32), (7, 96), (64, 512), (300, 2080), (129, 5120)])
+def test_shapes_f16(q4lib, gpu, m, n, k):
+    w = synth.random_weights(m + n + k, n, k, "outlier")
+    x = synth.random_activations(m * 3 + k, m, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemv(q4lib, x, packed, n, k, "f16", gpu)
+    assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")
+
+
+@pytest.mark.parametrize("xdt,ydt", [("f32", "f32"), ("f32", "f16"), ("f16", "f32")])
+@pytest.mark.parametrize("m", [1, 4, 13, 32])
+def test_dtypes(q4lib, gpu, xdt, ydt, m):
+    n, k = 257, 1056
+    w = synth.random_weights(5, n, k, "student_t")
+    x = synth.random_activations(6 + m, m, k, xdt)
+    packed = oracle.quantize(w)
+    g = run_gemv(q4lib, x, packed, n, k, ydt, gpu)
+    assert_matmul_close(g, x, packed, n, k, what=f"{xdt}->{ydt} m{m}")
+
+
+def test_edge_case_weights(q4lib, gpu):
+    """Every quantiser corner case, including scales far above the fp16 weight range
+    (the GEMV keeps q - 8 exact and applies d in fp32)."""
+    n, k = 96, 32 * 24
+    w = synth.edge_case_weights(7, n, k)
+    x = synth.random_activations(8, 10, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemv(q4lib, x, packed, n, k, "f32", gpu)
+    assert_matmul_close(g, x, packed, n, k, what="edge")
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_workloads_full(q4lib, gpu, wid):
+    """Full-size decode workloads, every output checked, GPU-quantised weights."""
+    wl = synth.WORKLOADS[wid]
+    lin = wl.linears[0]
+    w = workload_weights_cached(wl, lin)
+    packed_d = q4lib.q4_quantize(to_dev(w, gpu))
+    packed = to_host(packed_d)
+    assert np.array_equal(packed[:64], oracle.quantize(w[:64]))
+    del w
+    for m in wl.ms:
+        x = synth.workload_activations(wl, lin.k, m)
+        import torch
+        y = q4lib.q4_gemv(to_dev(x, gpu), packed_d,
+                          y_dtype=torch.float16 if wl.y_dtype == "f16" else torch.float32)
+        assert_matmul_close(to_host(y), x, packed, lin.n, lin.k, what=f"{wl.name} m{m}")
+
+
+def test_layer_workload_sampled(q4lib, gpu):
+    """All seven linears of the Student-t layer at M = 1 and 10, sampled outputs."""
+    import torch
+    wl = synth.WORKLOADS[5]
+    rng = np.random.default_rng(0)
+    for lin in wl.linears:
+        w = workload_weights_cached(wl, lin)
+        packed_d = q4lib.q4_quantize(to_dev(w, gpu))
+        packed = to_host(packed_d)
+        del w
+        cols = np.sort(rng.choice(lin.n, size=min(lin.n, 1024), replace=False))
+        cols[-1] = lin.n - 1
+        for m in (1, 10):
+            x = synth.workload_activations(wl, lin.k, m)
+            y = to_host(q4lib.q4_gemv(to_dev(x, gpu), packed_d, y_dtype=torch.float16))
+            assert_matmul_close(y[:, cols], x, packed, lin.n, lin.k, cols=cols,
+                                what=f"layer/{lin.name} m{m}")
+
+
+def test_deterministic(q4lib, gpu):
+    import torch
+    n, k = 5120, 5120
+    packed = q4lib.q4_quantize(to_dev(synth.random_weights(2, n, k, "student_t"), gpu))
+    for m in (1, 10, 32):
+        x = to_dev(synth.random_activations(m, m, k, "f16"), gpu)
+        a = to_host(q4lib.q4_gemv(x, packed, y_dtype=torch.float32))
+        b = to_host(q4lib.q4_gemv(x, packed, y_dtype=torch.float32))
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_sliced_activation_rows(q4lib, gpu):
+    """A batch given as a row slice of a bigger activation buffer (pointer offset)."""
+    import torch
+    n, k = 384, 512
+    w = synth.random_weights(4, n, k)
+    packed = oracle.quantize(w)
+    xall = synth.random_activations(9, 40, k, "f16")
+    xd = to_dev(xall, gpu)
+    y = q4lib.q4_gemv(xd[8:24], to_dev(packed, gpu), y_dtype=torch.float32)
+    assert_matmul_close(to_host(y), xall[8:24], packed, n, k, what="slice")

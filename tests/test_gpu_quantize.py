@@ -1,0 +1,73 @@
+"""GPU quantiser parity: packed bytes bit-identical to the oracle's."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _golden import load
+from _gpu import to_dev, to_host, workload_weights_cached
+
+pytestmark = pytest.mark.gpu
+
+BLOCKS, _ = load()
+
+
+def gpu_quantize(q4, w, dev):
+    return to_host(q4.q4_quantize(to_dev(w, dev)))
+
+
+def test_golden_blocks(q4lib, gpu):
+    w = np.stack([b.x for b in BLOCKS])
+    packed = gpu_quantize(q4lib, w, gpu)
+    for i, b in enumerate(BLOCKS):
+        assert packed[i].tobytes().hex() == b.hex, b.name
+
+
+def test_golden_blocks_fp16(q4lib, gpu):
+    rows = [b for b in BLOCKS if np.array_equal(b.x.astype(np.float16).astype(np.float32), b.x)]
+    w = np.stack([b.x for b in rows]).astype(np.float16)
+    packed = gpu_quantize(q4lib, w, gpu)
+    for i, b in enumerate(rows):
+        assert packed[i].tobytes().hex() == b.hex, b.name
+
+
+@pytest.mark.parametrize("n,k", [(1, 32), (3, 96), (17, 512), (64, 5120), (5, 17408), (33, 2080)])
+@pytest.mark.parametrize("dist", ["normal", "outlier", "student_t"])
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_shapes(q4lib, gpu, n, k, dist, dt):
+    w = synth.random_weights(n + k, n, k, dist)
+    if dt == "f16":
+        w = w.astype(np.float16)
+    assert np.array_equal(gpu_quantize(q4lib, w, gpu), oracle.quantize(w))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_edge_case_blocks(q4lib, gpu, dt):
+    w = synth.edge_case_weights(4, 96, 32 * 40, top=65504.0 if dt == "f16" else 5.0e5)
+    if dt == "f16":
+        w = w.astype(np.float16)
+    got = gpu_quantize(q4lib, w, gpu)
+    want = oracle.quantize(w)
+    bad = np.nonzero(np.any(got.reshape(-1, 18) != want.reshape(-1, 18), axis=1))[0]
+    assert bad.size == 0, f"{bad.size} blocks differ, first {bad[:5]}"
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_workload_weights_bit_exact(q4lib, gpu, wid):
+    """Every packed byte of every workload's weights, at full size."""
+    wl = synth.WORKLOADS[wid]
+    for lin in wl.linears:
+        w = workload_weights_cached(wl, lin)
+        got = gpu_quantize(q4lib, w, gpu)
+        step = 2048
+        for r0 in range(0, lin.n, step):
+            want = oracle.quantize(w[r0:r0 + step])
+            assert np.array_equal(got[r0:r0 + step], want), f"{wl.name}/{lin.name} rows {r0}+"
+
+
+def test_deterministic(q4lib, gpu):
+    w = to_dev(synth.random_weights(1, 256, 5120, "student_t"), gpu)
+    a = to_host(q4lib.q4_quantize(w))
+    b = to_host(q4lib.q4_quantize(w))
+    assert np.array_equal(a, b)
