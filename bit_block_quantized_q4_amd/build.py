@@ -31,6 +31,8 @@ COMMON_FLAGS = [
     "-Wno-unused-command-line-argument",
     # Disable packed fp32 instructions in device code (v_pk_*_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core results go straight to VGPRs (no accumulator-register copies).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]
