@@ -31,11 +31,17 @@ COMMON_FLAGS = [
     "-Wno-unused-command-line-argument",
     # Disable packed fp32 instructions in device code (v_pk_*_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # Matrix-core results go straight to VGPRs (no accumulator-register copies).
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]
+
+
+# Extra flags per translation unit.  The decode GEMV keeps its small matrix
+# products in ordinary VGPRs (no accumulator-register copies); the GEMM keeps
+# its large accumulators in AGPRs (the default form).
+PER_FILE_FLAGS = {
+    "q4_gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _hipcc() -> str:
@@ -72,7 +78,8 @@ def build(verbose: bool = False) -> Path:
     objs = [BUILD_DIR / (s.stem + ".o") for s in srcs]
     jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [hipcc, *COMMON_FLAGS, "-c", str(s), "-o", str(o)], verbose)
+        futs = [ex.submit(_run, [hipcc, *COMMON_FLAGS, *PER_FILE_FLAGS.get(s.name, []),
+                                 "-c", str(s), "-o", str(o)], verbose)
                 for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()

@@ -1,0 +1,102 @@
+// Device helpers shared by the libq4 kernels (gfx950).  Internal header.
+#pragma once
+
+#include "q4_internal.hpp"
+
+namespace q4 {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Bit patterns used by the unpack.  They are kept in registers (see
+// UnpackConsts) because VOP3 instructions cannot encode literals on gfx9, and
+// v_and_or_b32 needs all three operands in registers.
+struct UnpackConsts {
+  uint32_t mask_lo, mask_hi;  // 0x000F000F, 0x00F000F0
+  uint32_t exp_lo, exp_hi;    // fp16 1024 (0x6400) and 64 (0x5400) in both halves
+};
+
+__device__ __forceinline__ UnpackConsts make_unpack_consts() {
+  UnpackConsts k{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+  asm volatile("" : "+s"(k.mask_lo), "+s"(k.mask_hi), "+v"(k.exp_lo), "+v"(k.exp_hi));
+  return k;
+}
+
+// Exact fp16 (q - 8) for the eight codes of bytes c0..c3 taken from the 8-byte
+// LDS window {w1:w0} at byte offset O, in operand order
+// (e0, e1, e2, e3, e16, e17, e18, e19) relative to the lane's element base:
+// low nibble q becomes fp16 1024 + q and high nibble q becomes 64 + q (the
+// nibble lands in the low mantissa bits of a fixed exponent), then one exact
+// packed subtraction of 1032 / 72 leaves q - 8.
+template <int O>
+__device__ __forceinline__ half8_t unpack8(uint32_t w0, uint32_t w1, const UnpackConsts& k) {
+  constexpr uint32_t sel01 = (O + 0) | (0x0cu << 8) | ((O + 1u) << 16) | (0x0cu << 24);
+  constexpr uint32_t sel23 = (O + 2) | (0x0cu << 8) | ((O + 3u) << 16) | (0x0cu << 24);
+  const uint32_t t01 = __builtin_amdgcn_perm(w1, w0, sel01);  // [c0, 0, c1, 0]
+  const uint32_t t23 = __builtin_amdgcn_perm(w1, w0, sel23);  // [c2, 0, c3, 0]
+  const half2_t lo01 = __builtin_bit_cast(half2_t, (t01 & k.mask_lo) | k.exp_lo);
+  const half2_t lo23 = __builtin_bit_cast(half2_t, (t23 & k.mask_lo) | k.exp_lo);
+  const half2_t hi01 = __builtin_bit_cast(half2_t, (t01 & k.mask_hi) | k.exp_hi);
+  const half2_t hi23 = __builtin_bit_cast(half2_t, (t23 & k.mask_hi) | k.exp_hi);
+  const half2_t klo = {static_cast<half_t>(-1032.0f), static_cast<half_t>(-1032.0f)};
+  const half2_t khi = {static_cast<half_t>(-72.0f), static_cast<half_t>(-72.0f)};
+  const half2_t a = lo01 + klo, b = lo23 + klo, c = hi01 + khi, d = hi23 + khi;
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, a);
+  r[1] = __builtin_bit_cast(uint32_t, b);
+  r[2] = __builtin_bit_cast(uint32_t, c);
+  r[3] = __builtin_bit_cast(uint32_t, d);
+  return __builtin_bit_cast(half8_t, r);
+}
+
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// 16-byte global -> LDS copy for every active lane: lane l's bytes land at
+// lds + 16 * l (the LDS base, held in M0, must be uniform across the wave).
+// Issued as inline asm so that the compiler tracks no LDS-DMA writes of its
+// own: every wait on these copies is the explicit wait_vm below.
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lptr_t)(lds)));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+// Emitted through the s_waitcnt builtin (not inline asm) so that the
+// compiler's own wait tracking knows the counter has drained and does not
+// add a later wait that would also cover copies issued after this point.
+// The fence keeps LDS reads of the awaited data below it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4] = 7, lgkmcnt[11:8] = 15
+  constexpr int kImm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  __builtin_amdgcn_s_waitcnt(kImm);
+  asm volatile("" ::: "memory");
+}
+
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+// Register loads the compiler does not track (inline asm): the caller must
+// drain them with wait_vm and tie the results to that wait (see tie_after)
+// before reading them.  Used where copies into LDS and register loads share
+// one explicit wait, so that no compiler-inserted wait drains both.
+__device__ __forceinline__ u32x3 load_dwordx3_untracked(const void* p) {
+  u32x3 v;
+  asm volatile("global_load_dwordx3 %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+__device__ __forceinline__ uint32_t load_ushort_untracked(const void* p) {
+  uint32_t v;
+  asm volatile("global_load_ushort %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+// Make `v` depend on a point after an explicit wait, so its readers cannot be
+// scheduled above that wait.
+template <typename T>
+__device__ __forceinline__ void tie_after(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+
+}  // namespace q4

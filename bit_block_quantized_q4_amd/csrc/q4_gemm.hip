@@ -2,12 +2,29 @@
 //
 // The "GPU Q4_0 -> Tensor Core path" of the vertical-disaggregation page
 // (section "Every cycle counts: custom kernels"): long prompts are dense
-// computation, so the weight tiles are dequantised once per workgroup into
-// LDS as fp16 w = (q - 8) * d (one rounding) and contracted with the fp16
-// activations on v_mfma_f32_32x32x16_f16 with fp32 accumulation.  Each output
-// element is owned by exactly one lane and accumulated in a fixed k order, so
-// results are bit-reproducible.
-#include "q4_internal.hpp"
+// computation, so weight tiles are dequantised once per workgroup into LDS as
+// fp16 w = (q - 8) * d (one rounding) and contracted with the fp16 activations
+// on v_mfma_f32_32x32x16_f16 with fp32 accumulation.  Each output element is
+// owned by exactly one lane and accumulated in a fixed k order, so results are
+// bit-reproducible.
+//
+// Tiled kernel (k % 64 == 0)
+// --------------------------
+// A BM x BN output tile per workgroup of four wavefronts (2 x 2, each
+// BM/2 x BN/2), k steps of 64 (two Q4_0 blocks), two LDS stages:
+//   - activations: direct global->LDS copies (global_load_lds_dwordx4) of the
+//     BM x 64 fp16 tile, 16-byte pieces placed with an XOR swizzle
+//     (piece c of row r at r*8 + (c ^ (r & 7))) so that matrix-core operand
+//     reads hit distinct banks;
+//   - weights: each thread owns "units" of 8 code bytes of one row and one
+//     block (16 weights); the packed bytes of step s+1 are loaded into
+//     registers during step s-1..s, dequantised with byte permutes, the
+//     1024+q / 64+q exponent trick, an exact packed subtraction and one packed
+//     multiply by d, and written to the other stage in the same swizzle;
+//   - one barrier per k step; the step's matrix products interleave with the
+//     next step's dequantisation.
+// The generic kernel below handles k % 64 != 0.
+#include "q4_device.hpp"
 
 namespace q4 {
 namespace {
@@ -116,6 +133,226 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
       }
 }
 
+
+// ------------------------------------------------------------------ tiled
+
+constexpr int kBK = 64;            // k per step: two Q4_0 blocks
+constexpr int kRowBytes16 = 128;   // one tile row of 64 fp16 = 8 pieces of 16 bytes
+
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+
+// One weight unit: 8 code bytes (half h of block b of a row) and the scale.
+struct WUnit {
+  u32x3 w;     // 12-byte window that contains the 8 code bytes
+  uint32_t d;  // fp16 scale in the low half
+};
+
+template <int BM, int BN, typename YT>
+__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
+    const half_t* __restrict__ x, const uint8_t* __restrict__ W, YT* __restrict__ y,
+    int64_t m, int64_t n, int64_t k) {
+  constexpr int WM = BM / 2, WN = BN / 2;   // wave tile
+  constexpr int TM = WM / 32, TN = WN / 32; // 32 x 32 products per wave
+  constexpr int A_STAGE = BM * kRowBytes16;
+  constexpr int B_STAGE = BN * kRowBytes16;
+  constexpr int STAGE = A_STAGE + B_STAGE;
+  constexpr int A_COPIES = BM * 8 / 256;    // 16-byte copies per thread per step
+  constexpr int UNITS = BN * 4 / 256;       // weight units per thread per step
+  static_assert(A_COPIES >= 1 && UNITS >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
+  const int64_t rb = (k / kQK) * kBlockBytes;
+  const int nks = static_cast<int>(k / kBK);
+
+  // Activation copies: copy i of this thread is LDS piece P = 256 i + tid
+  // (row P / 8, swizzled column P % 8); the source column undoes the swizzle.
+  const half_t* asrc[A_COPIES];
+#pragma unroll
+  for (int i = 0; i < A_COPIES; ++i) {
+    const int P = 256 * i + tid;
+    const int r = P >> 3;
+    const int c = (P & 7) ^ (r & 7);
+    const int64_t row = m0 + r < m ? m0 + r : m - 1;
+    asrc[i] = x + row * k + 8 * c;
+  }
+  auto issue_a = [&](int ks, int stage) {
+    uint8_t* dst = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_COPIES; ++i)
+      dma16(asrc[i] + static_cast<int64_t>(ks) * kBK, dst + (256 * i + 64 * wave) * 16);
+  };
+
+  // Weight units: unit u of this thread is U = 256 u + tid: row U / 4,
+  // block (U / 2) % 2 of the step, half U % 2 (code bytes 8h .. 8h+7).
+  const uint8_t* wsrc[UNITS];
+  const uint16_t* dsrc[UNITS];
+  uint32_t sel_even[UNITS], sel_odd[UNITS];
+  int wrow[UNITS], wpiece_lo[UNITS];
+#pragma unroll
+  for (int u = 0; u < UNITS; ++u) {
+    const int U = 256 * u + tid;
+    const int r = U >> 2;
+    const int b = (U >> 1) & 1;
+    const int h = U & 1;
+    const int64_t row = n0 + r < n ? n0 + r : n - 1;
+    const int64_t boff = row * rb + b * kBlockBytes;  // + 36 per step
+    const int64_t coff = boff + 2 + 8 * h;             // first code byte
+    // 12-byte aligned window holding the 8 code bytes at offset sh; it stays
+    // within the 36 bytes of the step (rows are 36-byte multiples here):
+    // aligned code bytes (coff % 4 == 0) take the window 4 bytes earlier.
+    const int sh = (coff & 3) ? 2 : 4;
+    wsrc[u] = W + (coff - sh);
+    dsrc[u] = reinterpret_cast<const uint16_t*>(W + boff);
+    // pair i' of the unit: window bytes sh + 2 i' and + 1, within dwords
+    // i'/2 .. i'/2 + 1; selectors for even / odd i' pick them as [c, 0, c', 0].
+    const uint32_t s0 = static_cast<uint32_t>(sh);
+    const uint32_t s1 = static_cast<uint32_t>(sh + 2);
+    sel_even[u] = s0 | (0x0cu << 8) | ((s0 + 1) << 16) | (0x0cu << 24);
+    sel_odd[u] = s1 | (0x0cu << 8) | ((s1 + 1) << 16) | (0x0cu << 24);
+    wrow[u] = r;
+    wpiece_lo[u] = 4 * b + h;  // piece of the low nibbles; high nibbles: + 2
+  }
+  // Untracked loads of the packed bytes of step ks (see load_dwordx3_untracked).
+  struct Units {
+    WUnit v[UNITS];
+  };
+  auto load_units = [&](int ks) {
+    Units r;
+#pragma unroll
+    for (int u = 0; u < UNITS; ++u) {
+      r.v[u].w = load_dwordx3_untracked(wsrc[u] + static_cast<int64_t>(ks) * 2 * kBlockBytes);
+      r.v[u].d = load_ushort_untracked(dsrc[u] + static_cast<int64_t>(ks) * kBlockBytes);
+    }
+    return r;
+  };
+  auto tie_units = [&](Units& r) {
+#pragma unroll
+    for (int u = 0; u < UNITS; ++u) {
+      tie_after(r.v[u].w);
+      tie_after(r.v[u].d);
+    }
+  };
+
+  const UnpackConsts kc = make_unpack_consts();
+  // Dequantise unit u (16 weights) and store its two pieces into `stage`.
+  auto dequant_store = [&](const WUnit& un, int u, int stage) {
+    const half2_t d2 = __builtin_bit_cast(half2_t, (un.d & 0xFFFFu) | (un.d << 16));
+    const half2_t klo = {static_cast<half_t>(-1032.0f), static_cast<half_t>(-1032.0f)};
+    const half2_t khi = {static_cast<half_t>(-72.0f), static_cast<half_t>(-72.0f)};
+    u32x4 lo, hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t t = __builtin_amdgcn_perm(un.w[i / 2 + 1], un.w[i / 2],
+                                               (i & 1) ? sel_odd[u] : sel_even[u]);
+      const half2_t ql = __builtin_bit_cast(half2_t, (t & kc.mask_lo) | kc.exp_lo) + klo;
+      const half2_t qh = __builtin_bit_cast(half2_t, (t & kc.mask_hi) | kc.exp_hi) + khi;
+      lo[i] = __builtin_bit_cast(uint32_t, ql * d2);
+      hi[i] = __builtin_bit_cast(uint32_t, qh * d2);
+    }
+    uint8_t* bs = smem + stage * STAGE + A_STAGE;
+    *reinterpret_cast<u32x4*>(bs + swz(wrow[u], wpiece_lo[u]) * 16) = lo;
+    *reinterpret_cast<u32x4*>(bs + swz(wrow[u], wpiece_lo[u] + 2) * 16) = hi;
+  };
+
+  float16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Every vector-memory operation in the loop is untracked by the compiler
+  // (LDS copies and register loads); each step ends with one explicit drain.
+  // Prologue: stage 0 complete, packed weights of step 1 in registers.
+  issue_a(0, 0);
+  {
+    Units u0 = load_units(0);
+    wait_vm<0>();
+    tie_units(u0);
+#pragma unroll
+    for (int u = 0; u < UNITS; ++u) dequant_store(u0.v[u], u, 0);
+  }
+  Units nxt = load_units(nks > 1 ? 1 : 0);
+  wait_vm<0>();
+  tie_units(nxt);
+  __syncthreads();
+
+  const int arow = wm * WM + (lane & 31);
+  const int brow = wn * WN + (lane & 31);
+  const int kg = lane >> 5;
+
+  for (int ks = 0; ks < nks; ++ks) {
+    const int st = ks & 1;
+    const bool more = ks + 1 < nks;
+    if (more) issue_a(ks + 1, st ^ 1);
+    const Units cur = nxt;
+    nxt = load_units(ks + 2 < nks ? ks + 2 : nks - 1);
+    const uint8_t* as = smem + st * STAGE;
+    const uint8_t* bs = as + A_STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {  // 16-wide k sub-steps
+      half8_t af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const half8_t*>(as + swz(arow + 32 * i, 2 * kk + kg) * 16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bf[j] = *reinterpret_cast<const half8_t*>(bs + swz(brow + 32 * j, 2 * kk + kg) * 16);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      // Interleave the next step's dequantisation with the products.
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u)
+          if (u % 4 == kk) dequant_store(cur.v[u], u, st ^ 1);
+      }
+    }
+    wait_vm<0>();
+    tie_units(nxt);
+    __syncthreads();
+  }
+
+  // 32x32 accumulator layout: lane l holds column l % 32; register r holds
+  // row 8 * (r / 4) + 4 * (l / 32) + r % 4.
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * WM + 32 * i + 8 * (r / 4) + 4 * kg + (r & 3);
+        const int64_t col = n0 + wn * WN + 32 * j + (lane & 31);
+        if (row < m && col < n) y[row * n + col] = static_cast<YT>(acc[i][j][r]);
+      }
+}
+
+template <int BM, int BN, typename YT>
+hipError_t launch_tiled(const half_t* x, const uint8_t* packed, YT* y, int64_t m, int64_t n,
+                        int64_t k, hipStream_t s) {
+  void* argv[] = {const_cast<const half_t**>(&x), const_cast<const uint8_t**>(&packed), &y, &m,
+                  &n, &k};
+  const dim3 grid(static_cast<unsigned>((n + BN - 1) / BN), static_cast<unsigned>((m + BM - 1) / BM));
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, YT>), grid,
+                         dim3(256), argv, 0, s);
+}
+
+template <typename YT>
+hipError_t dispatch_tiled(const half_t* x, const uint8_t* packed, YT* y, int64_t m, int64_t n,
+                          int64_t k, hipStream_t s) {
+  if (m >= 1024) return launch_tiled<256, 256, YT>(x, packed, y, m, n, k, s);
+  return launch_tiled<128, 128, YT>(x, packed, y, m, n, k, s);
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
@@ -124,6 +361,10 @@ hipError_t launch_gemm(const void* x, DType, const uint8_t* packed, void* y,
                        DType yt, int64_t m, int64_t n, int64_t k, void*,
                        hipStream_t s) {
   const half_t* xp = static_cast<const half_t*>(x);
+  if (k % kBK == 0) {
+    if (yt == DType::F16) return dispatch_tiled(xp, packed, static_cast<half_t*>(y), m, n, k, s);
+    return dispatch_tiled(xp, packed, static_cast<float*>(y), m, n, k, s);
+  }
   const dim3 grid(static_cast<unsigned>((n + BN - 1) / BN),
                   static_cast<unsigned>((m + BM - 1) / BM));
   if (yt == DType::F16) {
