@@ -5,15 +5,23 @@ Headline: batched-decode GEMV weight GB/s on the 5120 x 5120 attention
 projection (M = 1, 4, 10, 16 per step, fp16 activations, fp16 output), with
 the packed weights rotated over >= 1 GiB of distinct copies so every launch
 streams from HBM rather than the 256 MB last-level cache.  One step = one
-GEMV launch per batch size, each on its own weight copy.
+GEMV launch per batch size, each on its own weight copy.  The W warm-up steps
+and the K timed steps are each recorded into a HIP graph and replayed, so the
+HIP events around the replay time GPU work, not Python's launch latency.
 
 The same JSON line carries:
-  roofline      -- the dominant GEMV launch: weight bytes / mean launch time
-                   (HIP events on the launch stream) against 8 TB/s HBM;
+  roofline      -- the step's dominant GEMV launch (K launches of that batch
+                   size back to back): algorithmic bytes (packed weights + x +
+                   y) / mean launch time, against 8 TB/s HBM; `traffic` is the
+                   HBM bytes per launch from the committed counter passes;
   gemm          -- prefill GEMM on the 2048 x 17408 x 5120 workload, whole
                    batch and 8 chunks of 256 rows, TFLOP/s against fp16 MFMA;
   quantize      -- the quantiser on the same 5120 x 5120 fp32 weight;
   cpu_baseline  -- the CPU oracle timed on a bounded sample of the step.
+
+Counter passes (HBM traffic): run `bench.py --traffic` once under
+`rocprofv3 --pmc FETCH_SIZE` and once under `--pmc WRITE_SIZE`, then
+`bench.py --traffic-summary FETCH.csv WRITE.csv` writes profiles/traffic.json.
 
 Run: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -62,11 +70,30 @@ def load_traffic(kernel_key: str):
     return data.get("kernels", {}).get(kernel_key)
 
 
-def events_elapsed_ms(pairs):
-    return [s.elapsed_time(e) for s, e in pairs]
+def capture(torch, fn):
+    """fn's launches recorded into a HIP graph (one eager call first warms them)."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
 
 
-def bench_gemv(q4, torch, dev, steps, warmup, rotate_bytes):
+def replay_seconds(torch, g):
+    """GPU time of one replay, from HIP events on the replay stream."""
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e-3
+
+
+def gemv_setup(q4, torch, dev, rotate_bytes):
     import synth
     wl = synth.WORKLOADS[2]
     lin = wl.linears[0]
@@ -79,49 +106,55 @@ def bench_gemv(q4, torch, dev, steps, warmup, rotate_bytes):
     ms = list(wl.ms)
     x = torch.from_numpy(synth.workload_activations(wl, k, max(ms))).to(dev)
     ys = {m: torch.empty((m, n), dtype=torch.float16, device=dev) for m in ms}
+    del wd
     torch.cuda.synchronize()
+    return {"wl": wl, "n": n, "k": k, "wbytes": wbytes, "w_host": w, "ncopies": ncopies,
+            "packed": packed, "ms": ms, "x": x, "ys": ys}
 
-    launch = [0]
 
-    def step(record=None):
-        for m in ms:
-            p = packed[launch[0] % ncopies]
-            launch[0] += 1
-            if record is not None:
-                s = torch.cuda.Event(enable_timing=True)
-                e = torch.cuda.Event(enable_timing=True)
-                s.record()
-            q4.q4_gemv(x[:m], p, y=ys[m])
-            if record is not None:
-                e.record()
-                record[m].append((s, e))
+def gemv_launches(q4, s, nsteps, ms, first):
+    """nsteps steps of one launch per batch size in ms, each launch on the next
+    weight copy (so no launch finds its weights in the last-level cache)."""
+    def fn():
+        i = first
+        for _ in range(nsteps):
+            for m in ms:
+                q4.q4_gemv(s["x"][:m], s["packed"][i % s["ncopies"]], y=s["ys"][m])
+                i += 1
+    return fn
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    rec = {m: [] for m in ms}
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step(rec)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
+def gemv_alg_bytes(m, n, k):
+    """Bytes a launch must move at least once: packed weights, x (fp16), y (fp16)."""
+    return n * (k // QK) * BLOCK_BYTES + 2 * m * k + 2 * m * n
+
+
+def bench_gemv(q4, torch, dev, steps, warmup, rotate_bytes):
+    s = gemv_setup(q4, torch, dev, rotate_bytes)
+    n, k, ms, wbytes = s["n"], s["k"], s["ms"], s["wbytes"]
+    # The whole step (all batch sizes), K steps in one graph after W warm-up steps.
+    gw = capture(torch, gemv_launches(q4, s, max(warmup, 1), ms, 0))
+    gt = capture(torch, gemv_launches(q4, s, steps, ms, max(warmup, 1) * len(ms)))
+    gw.replay()
+    step_s = replay_seconds(torch, gt) / steps
+    del gw, gt
+    # Per batch size: K launches back to back, mean launch time.
     per_m = []
     for m in ms:
-        d = np.array(events_elapsed_ms(rec[m]))
-        avg_s = float(d.mean()) * 1e-3
+        g = capture(torch, gemv_launches(q4, s, steps, [m], 0))
+        g.replay()
+        avg_s = replay_seconds(torch, g) / steps
+        del g
+        alg = gemv_alg_bytes(m, n, k)
         per_m.append({
-            "m": m, "mean_us": avg_s * 1e6, "p10_us": float(np.percentile(d, 10)) * 1e3,
-            "p90_us": float(np.percentile(d, 90)) * 1e3,
-            "weight_gbs": wbytes / avg_s / 1e9,
-            "total_gbs": (wbytes + m * k * 2 + m * n * 2) / avg_s / 1e9,
-            "frac_hbm": wbytes / avg_s / 1e9 / HBM_PEAK_GBS,
+            "m": m, "mean_us": avg_s * 1e6, "weight_gbs": wbytes / avg_s / 1e9,
+            "alg_bytes": alg, "alg_gbs": alg / avg_s / 1e9,
+            "frac_hbm": alg / avg_s / 1e9 / HBM_PEAK_GBS,
         })
-    step_s = wall / steps
     return {
-        "wl": wl, "n": n, "k": k, "ms": ms, "wbytes": wbytes, "ncopies": ncopies,
+        "wl": s["wl"], "n": n, "k": k, "ms": ms, "wbytes": wbytes, "ncopies": s["ncopies"],
         "step_s": step_s, "value_gbs": wbytes * len(ms) / step_s / 1e9, "per_m": per_m,
-        "w_host": w, "packed0": packed[0],
+        "w_host": s["w_host"],
     }
 
 
@@ -131,28 +164,23 @@ def bench_quantize(q4, torch, dev, w_host, reps, rotate_bytes):
     copies = max(2, -(-rotate_bytes // in_bytes))
     ws = [torch.from_numpy(w_host).to(dev) for _ in range(copies)]
     out = torch.empty((n, (k // QK) * BLOCK_BYTES), dtype=torch.uint8, device=dev)
-    for i in range(3):
-        q4.q4_quantize(ws[i % copies], packed=out)
-    torch.cuda.synchronize()
-    pairs = []
-    for i in range(reps):
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
-        q4.q4_quantize(ws[i % copies], packed=out)
-        e.record()
-        pairs.append((s, e))
-    torch.cuda.synchronize()
-    avg_s = float(np.mean(events_elapsed_ms(pairs))) * 1e-3
+
+    def fn():
+        for i in range(reps):
+            q4.q4_quantize(ws[i % copies], packed=out)
+
+    g = capture(torch, fn)
+    g.replay()
+    avg_s = replay_seconds(torch, g) / reps
     alg = n * k * 4 + n * (k // QK) * BLOCK_BYTES
     gbs = alg / avg_s / 1e9
-    return {"workload": "quantize_fp32_5120x5120", "mean_us": avg_s * 1e6,
+    return {"workload": "quantize_fp32_5120x5120", "mean_us": avg_s * 1e6, "alg_bytes": alg,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
                          "traffic": load_traffic("quantize_fp32_5120x5120")}}
 
 
-def bench_gemm(q4, torch, dev, reps):
+def gemm_setup(q4, torch, dev):
     import synth
     wl = synth.WORKLOADS[4]
     lin = wl.linears[0]
@@ -162,9 +190,8 @@ def bench_gemm(q4, torch, dev, reps):
     del w
     x = torch.from_numpy(synth.workload_activations(wl, k, m)).to(dev)
     y = torch.empty((m, n), dtype=torch.float16, device=dev)
-    ws = q4.q4_gemm_workspace_size(m, n, k)
-    wsc = q4.q4_gemm_workspace_size(256, n, k)
-    work = torch.empty(max(ws, wsc, 1), dtype=torch.uint8, device=dev)
+    ws = max(q4.q4_gemm_workspace_size(m, n, k), q4.q4_gemm_workspace_size(256, n, k), 1)
+    work = torch.empty(ws, dtype=torch.uint8, device=dev)
 
     def whole():
         q4.q4_gemm(x, packed, y=y, workspace=work)
@@ -173,20 +200,19 @@ def bench_gemm(q4, torch, dev, reps):
         for c in range(8):
             q4.q4_gemm(x[c * 256:(c + 1) * 256], packed, y=y[c * 256:(c + 1) * 256], workspace=work)
 
+    return m, n, k, whole, chunks
+
+
+def bench_gemm(q4, torch, dev, reps):
+    m, n, k, whole, chunks = gemm_setup(q4, torch, dev)
     res = {}
     for name, fn, calls in (("whole_2048", whole, 1), ("chunked_8x256", chunks, 8)):
-        fn()
-        torch.cuda.synchronize()
-        pairs = []
-        for _ in range(reps):
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
-            s.record()
-            fn()
-            e.record()
-            pairs.append((s, e))
-        torch.cuda.synchronize()
-        avg_s = float(np.mean(events_elapsed_ms(pairs))) * 1e-3
+        def rep():
+            for _ in range(reps):
+                fn()
+        g = capture(torch, rep)
+        g.replay()
+        avg_s = replay_seconds(torch, g) / reps
         tf = 2.0 * m * n * k / avg_s / 1e12
         res[name] = {"mean_us": avg_s * 1e6, "launches": calls, "tflops": tf,
                      "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS}
@@ -198,6 +224,111 @@ def bench_gemm(q4, torch, dev, reps):
                      "unit": "TFLOP/s", "frac": best / MFMA_F16_PEAK_TFLOPS,
                      "traffic": load_traffic("gemm_2048x17408x5120")},
     }
+
+
+# ------------------------------------------------------------ HBM traffic
+
+TRAFFIC_CALIB_BYTES = 512 << 20
+
+
+def traffic_run(q4, torch, dev, rotate_bytes, launches=20):
+    """The launches the two counter passes (FETCH_SIZE, then WRITE_SIZE) read:
+    a plain device copy of known size (torch's negation kernel: reads and writes
+    TRAFFIC_CALIB_BYTES once), then the GEMV at every batch size, the
+    quantiser and the whole-batch GEMM, each repeated."""
+    src = torch.ones(TRAFFIC_CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    del src, dst
+    s = gemv_setup(q4, torch, dev, rotate_bytes)
+    for m in s["ms"]:
+        gemv_launches(q4, s, launches, [m], 0)()
+    torch.cuda.synchronize()
+    ws = [torch.from_numpy(s["w_host"]).to(dev) for _ in range(2)]
+    for i in range(launches):
+        q4.q4_quantize(ws[i % 2], packed=s["packed"][0])
+    del s, ws
+    torch.cuda.synchronize()
+    _, _, _, whole, _ = gemm_setup(q4, torch, dev)
+    for _ in range(3):
+        whole()
+    torch.cuda.synchronize()
+    print("traffic launches done", flush=True)
+
+
+def _pmc_rows(csv_path):
+    """(dispatch id, kernel name, counter, value) rows of a rocprofv3 counter CSV."""
+    import csv
+    rows = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+            cnt = r.get("Counter_Name") or r.get("Counter-Name") or ""
+            val = float(r.get("Counter_Value") or r.get("Counter-Value") or 0.0)
+            did = int(r.get("Dispatch_Id") or r.get("Dispatch-Id") or len(rows))
+            rows.append((did, name, cnt, val))
+    rows.sort()
+    return rows
+
+
+def traffic_summary(fetch_csv, write_csv, out_path):
+    """profiles/traffic.json from the two counter passes: per kernel, the median
+    FETCH_SIZE and WRITE_SIZE per dispatch (KiB), each scaled by known bytes /
+    counted bytes of the plain copy.  GEMV dispatches are attributed to batch
+    sizes by launch order (traffic_run launches them in WORKLOADS[2].ms order)."""
+    import synth
+    ms = list(synth.WORKLOADS[2].ms)
+
+    def classify(name):
+        if "neg_kernel" in name:
+            return "calib_copy"
+        if "gemv_stream_kernel" in name or "gemv_rowwave_kernel" in name:
+            return "gemv"
+        if "quantize_kernel" in name:
+            return "quantize_fp32_5120x5120"
+        if "gemm_mfma_kernelILi256" in name or "gemm_mfma_kernel<256" in name:
+            return "gemm_2048x17408x5120"
+        return None
+
+    def medians(path, counter):
+        by = {}
+        gemv = []
+        for did, name, cnt, val in _pmc_rows(path):
+            if cnt != counter:
+                continue
+            key = classify(name)
+            if key == "gemv":
+                gemv.append(val)
+            elif key:
+                by.setdefault(key, []).append(val)
+        if gemv:
+            per = len(gemv) // len(ms)
+            for i, m in enumerate(ms):
+                by[f"gemv_5120x5120_m{m}"] = gemv[i * per:(i + 1) * per]
+        return {k: float(np.median(v)) for k, v in by.items()}, {k: len(v) for k, v in by.items()}
+
+    fetch, nf = medians(fetch_csv, "FETCH_SIZE")
+    write, nw = medians(write_csv, "WRITE_SIZE")
+    f_scale = TRAFFIC_CALIB_BYTES / (fetch["calib_copy"] * 1024.0)
+    w_scale = TRAFFIC_CALIB_BYTES / (write["calib_copy"] * 1024.0)
+    kernels = {}
+    for key in sorted(set(fetch) & set(write)):
+        if key == "calib_copy":
+            continue
+        fb = fetch[key] * 1024.0 * f_scale
+        wb = write[key] * 1024.0 * w_scale
+        kernels[key] = {"fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb,
+                        "fetch_kib_raw": fetch[key], "write_kib_raw": write[key],
+                        "dispatches": min(nf[key], nw[key])}
+    data = {"source_hash": kernel_source_hash(),
+            "calibration": {"bytes": TRAFFIC_CALIB_BYTES, "fetch_kib": fetch["calib_copy"],
+                            "write_kib": write["calib_copy"], "fetch_scale": f_scale,
+                            "write_scale": w_scale},
+            "kernels": kernels}
+    Path(out_path).write_text(json.dumps(data, indent=1) + "\n")
+    return data
 
 
 def cpu_baseline(w_host, n, k, ms, budget_s=12.0):
@@ -236,7 +367,17 @@ def main():
     ap.add_argument("--gemm-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "gemv", "gemm", "quantize"], default="all")
+    ap.add_argument("--traffic", action="store_true",
+                    help="run the launches the FETCH_SIZE / WRITE_SIZE counter passes read")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from the two counter passes")
     args = ap.parse_args()
+
+    if args.traffic_summary:
+        d = traffic_summary(args.traffic_summary[0], args.traffic_summary[1],
+                            ROOT / "profiles" / "traffic.json")
+        print(json.dumps(d, indent=1))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the Q4_0 path has no multi-GPU leg "
@@ -251,10 +392,13 @@ def main():
     q4.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     rotate = args.rotate_mib << 20
+    if args.traffic:
+        traffic_run(q4, torch, dev, rotate)
+        return
 
     out = {"metric": METRIC}
     g = bench_gemv(q4, torch, dev, args.steps, args.warmup, rotate)
-    dom = max(g["per_m"], key=lambda r: r["mean_us"])
+    dom = max(g["per_m"], key=lambda r: r["mean_us"])  # the step's dominant launch
     out.update({
         "value": g["value_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": g["step_s"] * 1e3, "higher_is_better": True,
@@ -263,10 +407,11 @@ def main():
                    "x_dtype": "f16", "y_dtype": "f16",
                    "weight_copies_rotated": g["ncopies"],
                    "weight_bytes_per_launch": g["wbytes"]},
-        "roofline": {"bound": "hbm", "achieved": dom["weight_gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": dom["weight_gbs"] / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": dom["alg_gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": dom["alg_gbs"] / HBM_PEAK_GBS,
                      "traffic": load_traffic(f"gemv_5120x5120_m{dom['m']}"),
-                     "kernel": f"q4_gemv m={dom['m']}"},
+                     "kernel": f"q4_gemv m={dom['m']}", "mean_us": dom["mean_us"],
+                     "alg_bytes_per_launch": dom["alg_bytes"]},
         "per_m": g["per_m"],
     })
     if args.only in ("all", "quantize"):

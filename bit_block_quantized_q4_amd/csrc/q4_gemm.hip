@@ -1,6 +1,6 @@
 // Q4_0 prefill GEMM for gfx950: y[m][n] = x[m][k] . dequant(W)^T on fp16 MFMA.
 //
-// The "GPU Q4_0 -> Tensor Core path" of the vertical-disaggregation page
+// The GPU path from Q4_0 weights onto matrix cores of the vertical-disaggregation page
 // (section "Every cycle counts: custom kernels"): long prompts are dense
 // computation, so weight tiles are dequantised once per workgroup into LDS as
 // fp16 w = (q - 8) * d (one rounding) and contracted with the fp16 activations

@@ -1,6 +1,6 @@
 // Q4_0 batched-decode GEMV for gfx950: y[m][n] = x[m][k] . dequant(W)^T, m <= 32.
 //
-// The "batch decode" stage of the vertical-disaggregation page (section
+// The batched decode stage of the vertical-disaggregation page (section
 // "Every cycle counts: custom kernels"): many sessions' decode steps share one
 // pass over the weights, so each packed byte is read from HBM once for all m
 // activation rows.  Every output is the fp32 sum over blocks of d times the

@@ -103,7 +103,7 @@ q4_status q4_quantize(const void *w, int w_dtype, int64_t n, int64_t k,
                       void *packed, q4_stream_t stream);
 
 /* Batched-decode GEMV: y[m][n] = x[m][k] . dequant(packed)^T for
- * 1 <= m <= Q4_GEMV_MAX_M (the "batch decode" stage).  x is Q4_F32 or
+ * 1 <= m <= Q4_GEMV_MAX_M (the page's batched decode stage).  x is Q4_F32 or
  * Q4_F16, y is Q4_F32 or Q4_F16.  Every output is the fp32 sum over blocks of
  * d times the exact block dot product of x with (q - 8), rounded once to the
  * output dtype.  Streams each packed byte from memory once per call. */
@@ -115,7 +115,7 @@ q4_status q4_gemv(const void *x, int x_dtype, const void *packed, void *y,
 size_t q4_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 
 /* Prefill GEMM: y[m][n] = x[m][k] . dequant(packed)^T for any m >= 1 (the
- * "GPU Q4_0 -> Tensor Core path"): weight tiles are dequantised to fp16
+ * page's GPU path onto matrix cores): weight tiles are dequantised to fp16
  * (w = (q - 8) * d rounded once) and contracted on fp16 matrix cores with fp32
  * accumulation.  Because the weights are rounded to fp16, every block scale
  * must satisfy |d| <= 8188 (every dequantised weight within the fp16 range,

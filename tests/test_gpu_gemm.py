@@ -125,3 +125,27 @@ def test_largest_fp16_scale(q4lib, gpu):
     g = run_gemm(q4lib, x, packed, n, k, "f32", gpu)
     assert np.all(np.isfinite(g))
     assert_matmul_close(g, x, packed, n, k, what="largest scale")
+
+
+def test_graph_replay_matches_eager(q4lib, gpu):
+    """A graph of GEMM launches (as the benchmark times them) reproduces the
+    eager result on every replay."""
+    import torch
+    m, n, k = 300, 384, 1024
+    w = synth.random_weights(43, n, k, "normal")
+    packed = to_dev(oracle.quantize(w), gpu)
+    x = to_dev(synth.random_activations(44, m, k, "f16"), gpu)
+    eager = to_host(q4lib.q4_gemm(x, packed, n=n, k=k))
+    work = torch.empty(max(q4lib.q4_gemm_workspace_size(m, n, k), 1), dtype=torch.uint8,
+                       device=gpu)
+    y = torch.empty((m, n), dtype=torch.float16, device=gpu)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q4lib.q4_gemm(x, packed, y=y, workspace=work, n=n, k=k)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(y), eager), f"replay {rep}"

@@ -134,3 +134,31 @@ def test_sliced_activation_rows(q4lib, gpu):
     xd = to_dev(xall, gpu)
     y = q4lib.q4_gemv(xd[8:24], to_dev(packed, gpu), y_dtype=torch.float32)
     assert_matmul_close(to_host(y), xall[8:24], packed, n, k, what="slice")
+
+
+def test_graph_replay_matches_eager(q4lib, gpu):
+    """Launches recorded into a HIP graph (as the benchmark times them) give the
+    eager result on every replay, with eager work and synchronisation between
+    replays."""
+    import torch
+    n, k = 520, 2048
+    w = synth.random_weights(41, n, k, "outlier")
+    packed = to_dev(oracle.quantize(w), gpu)
+    xs = {m: to_dev(synth.random_activations(40 + m, m, k, "f16"), gpu) for m in (1, 10, 16)}
+    eager = {m: to_host(q4lib.q4_gemv(xs[m], packed, n=n, k=k)) for m in xs}
+    ys = {m: torch.empty((m, n), dtype=torch.float16, device=gpu) for m in xs}
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for m in xs:
+            q4lib.q4_gemv(xs[m], packed, y=ys[m], n=n, k=k)
+    for rep in range(4):
+        for m in xs:
+            ys[m].fill_(float("nan"))
+        scratch = q4lib.q4_gemv(xs[16], packed, n=n, k=k)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for m in xs:
+            assert np.array_equal(to_host(ys[m]), eager[m]), f"replay {rep} m={m}"
+        assert np.array_equal(to_host(scratch), eager[16])
