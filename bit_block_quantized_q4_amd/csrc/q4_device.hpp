@@ -73,6 +73,15 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("" ::: "memory");
 }
 
+// As wait_vm, and also until every LDS operation of this wave has completed.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  constexpr int kImm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
+  __builtin_amdgcn_s_waitcnt(kImm);
+  asm volatile("" ::: "memory");
+}
+
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // Register loads the compiler does not track (inline asm): the caller must
@@ -87,6 +96,16 @@ __device__ __forceinline__ u32x3 load_dwordx3_untracked(const void* p) {
 __device__ __forceinline__ uint32_t load_ushort_untracked(const void* p) {
   uint32_t v;
   asm volatile("global_load_ushort %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+__device__ __forceinline__ u32x4 load_dwordx4_untracked(const void* p) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+__device__ __forceinline__ uint32_t load_dword_untracked(const void* p) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p));
   return v;
 }
 // Make `v` depend on a point after an explicit wait, so its readers cannot be

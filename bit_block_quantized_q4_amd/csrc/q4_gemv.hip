@@ -331,10 +331,341 @@ hipError_t dispatch_stream(const void* x, const uint8_t* packed, void* y, bool y
   return launch_stream<2, 32, 2, 4>(x, packed, y, y_f16, m, n, k, s);
 }
 
+// ----------------------------------------------------------------- balanced
+
+// Balanced kernel (fp16 activations, m <= 4, k % 512 == 0)
+// ----------------------------------------------------------
+// Rows are dealt out in groups of four, so every workgroup (one per compute
+// unit) owns the same number of rows: 5120 rows are 20 per unit, 17408 are 68,
+// 1024 are 4.  The products run on v_mfma_f32_4x4x4_16b_f16, sixteen
+// independent 4 x 4 x 4 products per instruction:
+//   lane l = 4 s + j holds slot s (operands A and B) and column j (B and D);
+//   A_s (4 x 4): activation row i = l % 4 (rows past m repeat row m - 1);
+//   B_s (4 x 4): weight row 4 rg + j, the same 4 elements, as exact (q - 8);
+//   D_s (4 x 4): lane l, register i = activation row i, column j.
+// Slot s is block s of a "set" of 16 consecutive blocks (512 values of k), so
+// lane l owns one whole Q4_0 block of one weight row per task (a task is one
+// row group of 4 rows times one set: 4 x 288 contiguous bytes).  Eight
+// chained instructions walk the block's 32 elements: instruction (u, h) takes
+// code bytes 4u .. 4u+3, low nibbles (elements 4u .. 4u+3) for h = 0 and high
+// nibbles (elements 4u+16 .. 4u+19) for h = 1, so its A operand is two
+// adjacent activation dwords.  The lane then scales the block product by its
+// own block's d with one fp32 FMA per activation row.
+//
+// Data movement is all 16-byte direct global->LDS copies, coalesced: the
+// workgroup first stages x (m rows of k halves), then each wave streams its
+// tasks through a private LDS ring of P slots (72 pieces per task: the four
+// 288-byte row segments).  Every task issues exactly two copies (past the
+// wave's last task the last one is copied again), so "task t has landed" is
+// always "at most 2 (P - 1) copies in flight".  Lanes read their block and
+// activations from LDS.  Tasks are numbered row-group-major and dealt to the
+// waves in contiguous ranges; a wave accumulates its current row group in registers and, when the
+// row group changes, folds the 16 slots per row of lanes with two row-shift
+// adds and stores the four row partials.  At the end every output sums the
+// row partials of the waves that touched its row group, in wave order.
+
+constexpr int kSetBlocks = 16;
+constexpr int kSetK = kSetBlocks * kQK;                   // 512
+constexpr int kTaskRowBytes = kSetBlocks * kBlockBytes;   // 288 = 18 pieces
+constexpr int kTaskBytes = 4 * kTaskRowBytes;             // 1152
+constexpr int kTaskPieces = kTaskBytes / 16;              // 72
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+// LDS layout of a workgroup (byte offsets); shared by the kernel and the host.
+struct BalLds {
+  int64_t x_ops;   // 16-byte copies per wave for x
+  int64_t x_bytes, ring_off, part_off, total;
+};
+__host__ __device__ inline BalLds bal_lds(int m, int64_t k, int rg, int nw, int p) {
+  BalLds L;
+  const int64_t pieces = (static_cast<int64_t>(m) * k * 2 + 15) / 16;
+  L.x_ops = (pieces + nw * kWave - 1) / (nw * kWave);
+  L.x_bytes = L.x_ops * nw * kWave * 16;
+  L.ring_off = L.x_bytes;
+  L.part_off = L.ring_off + static_cast<int64_t>(nw) * p * kTaskBytes;
+  // [row group][wave][lane row R][column j] float4 (zero where untouched)
+  L.total = L.part_off + static_cast<int64_t>(rg) * nw * 16 * 16;
+  return L;
+}
+
+template <int NW, int P>
+__global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
+    const half_t* __restrict__ x, const uint8_t* __restrict__ W, void* __restrict__ y,
+    int m, int64_t n, int64_t k, int rows_per_wg, int y_f16) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t bal_smem[];
+  const int lane = threadIdx.x & (kWave - 1);
+  // Wave-uniform (scalar) so that the task loop's control flow is uniform.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+  const int nrows = static_cast<int>(n - r0 < rows_per_wg ? n - r0 : rows_per_wg);
+  const int RG = (nrows + 3) >> 2;
+  const int S = static_cast<int>(k / kSetK);
+  const int T = RG * S;
+  const int t0 = static_cast<int>((static_cast<int64_t>(T) * wave) / NW);
+  const int t1 = static_cast<int>((static_cast<int64_t>(T) * (wave + 1)) / NW);
+  const int64_t rb = (k / kQK) * kBlockBytes;
+  const BalLds L = bal_lds(m, k, RG, NW, P);
+  uint8_t* const xs = bal_smem;
+  uint8_t* const ring = bal_smem + L.ring_off + static_cast<int64_t>(wave) * P * kTaskBytes;
+  float4_t* const part = reinterpret_cast<float4_t*>(bal_smem + L.part_off);
+  for (int i = threadIdx.x; i < RG * NW * 16; i += NW * kWave) part[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // x staging: wave w copies pieces (w * x_ops + q) * 64 + lane; pieces past
+  // the end re-read the last piece into the padding of the region.
+  {
+    const int64_t pieces = (static_cast<int64_t>(m) * k * 2 + 15) / 16;
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+    for (int64_t q = 0; q < L.x_ops; ++q) {
+      const int64_t blk = static_cast<int64_t>(wave) * L.x_ops + q;
+      int64_t pc = blk * kWave + lane;
+      if (pc > pieces - 1) pc = pieces - 1;
+      dma16(xb + 16 * pc, xs + blk * kWave * 16);
+    }
+  }
+
+  // Task copies: piece p = lane (first copy) and 64 + lane (second copy,
+  // lanes 0..7) of the 4 x 18 pieces; piece p is row p / 18, column p % 18.
+  const int pj0 = lane / 18, pc0 = lane - 18 * (lane / 18);
+  const int pj1 = (kWave + lane) / 18, pc1 = (kWave + lane) - 18 * ((kWave + lane) / 18);
+  auto issue_task = [&](int st, int rg, int slot) {
+    uint8_t* dst = ring + slot * kTaskBytes;
+    const int64_t base = static_cast<int64_t>(st) * kTaskRowBytes;
+    int64_t row0 = r0 + 4 * rg + pj0;
+    if (row0 > n - 1) row0 = n - 1;  // ragged last group: computed, never stored
+    dma16(W + row0 * rb + base + 16 * pc0, dst);
+    if (lane < kTaskPieces - kWave) {
+      int64_t row1 = r0 + 4 * rg + pj1;
+      if (row1 > n - 1) row1 = n - 1;
+      dma16(W + row1 * rb + base + 16 * pc1, dst + kWave * 16);
+    }
+  };
+
+  const int j = lane & 3;    // B/D column: weight row within the group; A row
+  const int sl = lane >> 2;  // slot: block within the set
+  const bool odd = (sl & 1) != 0;  // block parity (sets start on even blocks)
+  // Byte selectors on the window {w[u+1]:w[u]} of the lane's five dwords:
+  // code bytes 4u, 4u+1 (sel_a) and 4u+2, 4u+3 (sel_b) as [c, 0, c', 0]; code
+  // byte b sits at window offset b + 2 in an even block and b in an odd one.
+  // dsel picks the scale's two bytes.
+  const uint32_t sel_a = odd ? 0x0c010c00u : 0x0c030c02u;
+  const uint32_t sel_b = odd ? 0x0c030c02u : 0x0c050c04u;
+  const uint32_t dsel = odd ? 0x0c0c0706u : 0x0c0c0100u;
+  // The lane's five dwords in the slot: [w0..w3] from the block start (even
+  // block) or start + 2 (odd), and w4 at start + 16 (even) or start - 2 (odd);
+  // all inside the slot's row segment.
+  const int blk_off = kTaskRowBytes * j + kBlockBytes * sl;
+  const int off4 = blk_off + (odd ? 2 : 0);
+  const int off1 = blk_off + (odd ? -2 : 16);
+  const int mm = j < m ? j : m - 1;
+  const UnpackConsts kc = make_unpack_consts();
+  const half2_t klo = {static_cast<half_t>(-1032.0f), static_cast<half_t>(-1032.0f)};
+  const half2_t khi = {static_cast<half_t>(-72.0f), static_cast<half_t>(-72.0f)};
+
+  float4_t accr = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const uint8_t* slot, int st) {
+    const uint32_t* wv = reinterpret_cast<const uint32_t*>(slot + off4);
+    const uint32_t w0 = wv[0], w1 = wv[1], w2 = wv[2], w3 = wv[3];
+    const uint32_t w4 = *reinterpret_cast<const uint32_t*>(slot + off1);
+    const u32x4* xa = reinterpret_cast<const u32x4*>(
+        xs + (static_cast<int64_t>(mm) * k + static_cast<int64_t>(kSetBlocks * st + sl) * kQK) * 2);
+    const u32x4 xr[4] = {xa[0], xa[1], xa[2], xa[3]};
+    const float d = half_bits_to_float(static_cast<uint16_t>(__builtin_amdgcn_perm(w4, w0, dsel)));
+    float4_t D;
+    // A operand of (u, h): activation dwords 8h + 2u and 8h + 2u + 1.
+    auto a_op = [&](auto uu, auto hh) {
+      constexpr int dw = 8 * decltype(hh)::value + 2 * decltype(uu)::value;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 pr = {xr[dw >> 2][dw & 3], xr[dw >> 2][(dw & 3) + 1]};
+      return __builtin_bit_cast(half4_t, pr);
+    };
+    // Code dword u is the byte window {hi:lo} = {w[u + 1] : w[u]}.
+    auto dword = [&](auto uu, uint32_t hi, uint32_t lo) {
+      constexpr int u = decltype(uu)::value;
+      const uint32_t t01 = __builtin_amdgcn_perm(hi, lo, sel_a);
+      const uint32_t t23 = __builtin_amdgcn_perm(hi, lo, sel_b);
+      const half2_t l01 = __builtin_bit_cast(half2_t, (t01 & kc.mask_lo) | kc.exp_lo) + klo;
+      const half2_t l23 = __builtin_bit_cast(half2_t, (t23 & kc.mask_lo) | kc.exp_lo) + klo;
+      const half2_t h01 = __builtin_bit_cast(half2_t, (t01 & kc.mask_hi) | kc.exp_hi) + khi;
+      const half2_t h23 = __builtin_bit_cast(half2_t, (t23 & kc.mask_hi) | kc.exp_hi) + khi;
+      const half4_t Blo = {l01[0], l01[1], l23[0], l23[1]};
+      const half4_t Bhi = {h01[0], h01[1], h23[0], h23[1]};
+      D = __builtin_amdgcn_mfma_f32_4x4x4f16(a_op(uu, IC<0>{}), Blo,
+                                             u == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : D, 0, 0, 0);
+      D = __builtin_amdgcn_mfma_f32_4x4x4f16(a_op(uu, IC<1>{}), Bhi, D, 0, 0, 0);
+    };
+    dword(IC<0>{}, w1, w0);
+    dword(IC<1>{}, w2, w1);
+    dword(IC<2>{}, w3, w2);
+    dword(IC<3>{}, w4, w3);
+    accr = d * D + accr;
+  };
+
+  // Fold of the 16 slots per row of 16 lanes: after two row-shift adds lane
+  // 16 R + 12 + j holds the sum over slots 4R .. 4R+3 for weight row j.
+  // (The element is copied to a scalar before the bit cast: a bit cast of a
+  // vector element expression has been compiled as a read of element 0.)
+  auto dpp_add = [](float4_t v, auto ctrl) {
+    constexpr int c = decltype(ctrl)::value;
+    float4_t r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ve = v[e];
+      const int sh = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ve), c, 0xF, 0xF, true);
+      r[e] = ve + __builtin_bit_cast(float, sh);
+    }
+    return r;
+  };
+  auto flush = [&](int rg) {
+    float4_t v = dpp_add(accr, IC<0x118>{});  // row_shr:8
+    v = dpp_add(v, IC<0x114>{});               // row_shr:4
+    if ((lane & 15) >= 12) part[((rg * NW + wave) * 4 + (lane >> 4)) * 4 + (lane & 3)] = v;
+    accr = float4_t{0.f, 0.f, 0.f, 0.f};
+  };
+
+  if (t0 < t1) {
+    int lrg = t0 / S, lset = t0 - (t0 / S) * S, lt = t0;
+    auto next_copy = [&](int slot) {
+      issue_task(lset, lrg, slot);
+      if (lt < t1 - 1) {
+        ++lt;
+        if (++lset == S) { lset = 0; ++lrg; }
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < P; ++i) next_copy(i);
+    // This wave's x copies and partial-sum zeroing are complete; the barrier
+    // extends that to every wave.
+    wait_vm_lgkm0<2 * P>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    int cset = t0 - (t0 / S) * S, crg = t0 / S;
+    auto task = [&](int i) {
+      wait_vm<2 * (P - 1)>();
+      compiler_fence();
+      compute(ring + i * kTaskBytes, cset);
+      compiler_fence();  // the slot's reads are consumed above
+      next_copy(i);
+      if (++cset == S) {  // row group complete
+        cset = 0;
+        flush(crg);
+        ++crg;
+      }
+    };
+    // Whole rounds of P tasks (no exit inside a round), then the tail.
+    const int ntask = t1 - t0;
+    int done = 0;
+    for (; done + P <= ntask; done += P) {
+#pragma unroll
+      for (int i = 0; i < P; ++i) task(i);
+    }
+    const int rem = ntask - done;
+#pragma unroll
+    for (int i = 0; i < P - 1; ++i) {
+      if (i >= rem) break;
+      task(i);
+    }
+    if (cset != 0) flush(crg);  // the last row group was only partly this wave's
+    wait_vm<0>();  // drain the copies past the last task
+  } else {
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();  // matches the barrier of the waves with tasks
+  }
+
+  __syncthreads();
+  const int O = nrows * m;
+  const float* pf = reinterpret_cast<const float*>(part);
+  for (int o = threadIdx.x; o < O; o += NW * kWave) {
+    const int rl = o / m, mo = o - (o / m) * m;
+    const int rg = rl >> 2, jj = rl & 3;
+    const float* q = pf + static_cast<int64_t>(rg) * NW * 64 + jj * 4 + mo;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int R = 0; R < 4; ++R) sum += q[(w * 4 + R) * 16];
+    const int64_t off = static_cast<int64_t>(mo) * n + r0 + rl;
+    if (y_f16) static_cast<half_t*>(y)[off] = static_cast<half_t>(sum);
+    else static_cast<float*>(y)[off] = sum;
+  }
+}
+
+constexpr int64_t kLdsMax = 160 * 1024;
+constexpr int kBalP = 4;  // tasks in flight per wave
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+struct BalPlan {
+  int rows_per_wg = 0, grid = 0, nw = 0;
+  int64_t lds = 0;
+};
+
+// Rows per workgroup: a multiple of 4 near n / (compute units).  Returns false
+// when the shape is outside the kernel (the caller uses the other kernels).
+bool bal_plan(int m, int64_t n, int64_t k, BalPlan* p) {
+  if (m < 1 || m > 4 || k % kSetK != 0) return false;
+  const int64_t cu = device_cu_count();
+  const int64_t rows = 4 * ((n + 4 * cu - 1) / (4 * cu));
+  if (rows > (1 << 20)) return false;
+  p->rows_per_wg = static_cast<int>(rows);
+  p->grid = static_cast<int>((n + rows - 1) / rows);
+  const int rg = static_cast<int>(rows / 4);
+  for (int nw : {16, 8}) {
+    const BalLds L = bal_lds(m, k, rg, nw, kBalP);
+    if (L.total <= kLdsMax) {
+      p->nw = nw;
+      p->lds = L.total;
+      return true;
+    }
+  }
+  return false;
+}
+
+template <int NW>
+hipError_t launch_bal_t(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
+                        int64_t n, int64_t k, const BalPlan& p, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(&gemv_bal_kernel<NW, kBalP>);
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(kLdsMax));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const half_t* xp = static_cast<const half_t*>(x);
+  int rows = p.rows_per_wg, yf = y_f16 ? 1 : 0;
+  void* argv[] = {&xp, const_cast<const uint8_t**>(&packed), &y, &m, &n, &k, &rows, &yf};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(p.grid)), dim3(NW * kWave), argv,
+                         static_cast<size_t>(p.lds), s);
+}
+
+hipError_t dispatch_bal(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
+                        int64_t n, int64_t k, const BalPlan& p, hipStream_t s) {
+  if (p.nw == 16) return launch_bal_t<16>(x, packed, y, y_f16, m, n, k, p, s);
+  return launch_bal_t<8>(x, packed, y, y_f16, m, n, k, p, s);
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const void* x, DType xt, const uint8_t* packed, void* y,
                        DType yt, int m, int64_t n, int64_t k, hipStream_t s) {
+  BalPlan plan;
+  if (xt == DType::F16 && bal_plan(m, n, k, &plan))
+    return dispatch_bal(x, packed, y, yt == DType::F16, m, n, k, plan, s);
   if (xt == DType::F16 && stream_supports(k))
     return dispatch_stream(x, packed, y, yt == DType::F16, m, n, k, s);
   if (xt == DType::F16) {

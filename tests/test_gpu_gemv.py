@@ -162,3 +162,15 @@ def test_graph_replay_matches_eager(q4lib, gpu):
         for m in xs:
             assert np.array_equal(to_host(ys[m]), eager[m]), f"replay {rep} m={m}"
         assert np.array_equal(to_host(scratch), eager[16])
+
+
+@pytest.mark.parametrize("m", [1, 3, 4, 7, 12, 16])
+@pytest.mark.parametrize("n,k", [(4, 512), (5, 512), (1027, 1024), (2051, 3072), (6000, 1536)])
+def test_row_group_shapes(q4lib, gpu, m, n, k):
+    """Shapes around the four-row grouping: a single group, a ragged last group,
+    workgroups whose waves get no task, and task ranges spanning several sets."""
+    w = synth.random_weights(7 * m + n + k, n, k, "outlier")
+    x = synth.random_activations(5 * m + k, m, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemv(q4lib, x, packed, n, k, "f16", gpu)
+    assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")
