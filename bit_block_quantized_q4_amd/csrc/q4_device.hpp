@@ -82,6 +82,33 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   asm volatile("" ::: "memory");
 }
 
+// As wait_vm / wait_vm_lgkm0 for a run-time count n <= MAXN (a chain of
+// uniform compares choosing the immediate).
+template <int MAXN>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  if constexpr (MAXN == 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= MAXN) {
+      wait_vm<MAXN>();
+      return;
+    }
+    wait_vm_upto<MAXN - 1>(n);
+  }
+}
+template <int MAXN>
+__device__ __forceinline__ void wait_vm_lgkm0_upto(int n) {
+  if constexpr (MAXN == 0) {
+    wait_vm_lgkm0<0>();
+  } else {
+    if (n >= MAXN) {
+      wait_vm_lgkm0<MAXN>();
+      return;
+    }
+    wait_vm_lgkm0_upto<MAXN - 1>(n);
+  }
+}
+
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // Register loads the compiler does not track (inline asm): the caller must

@@ -355,14 +355,16 @@ hipError_t dispatch_stream(const void* x, const uint8_t* packed, void* y, bool y
 // Data movement is all 16-byte direct global->LDS copies, coalesced: the
 // workgroup first stages x (m rows of k halves), then each wave streams its
 // tasks through a private LDS ring of P slots (72 pieces per task: the four
-// 288-byte row segments).  Every task issues exactly two copies (past the
-// wave's last task the last one is copied again), so "task t has landed" is
-// always "at most 2 (P - 1) copies in flight".  Lanes read their block and
+// 288-byte row segments).  Every task issues exactly two copies and the
+// wave keeps at most P tasks in flight, so in steady state "task t has
+// landed" is "at most 2 (P - 1) copies in flight"; the last P tasks wait for
+// exact counts of the copies still behind them (no copies are wasted past the
+// wave's last task).  Lanes read their block and
 // activations from LDS.  Tasks are numbered row-group-major and dealt to the
-// waves in contiguous ranges; a wave accumulates its current row group in registers and, when the
-// row group changes, folds the 16 slots per row of lanes with two row-shift
-// adds and stores the four row partials.  At the end every output sums the
-// row partials of the waves that touched its row group, in wave order.
+// waves in contiguous ranges; a wave accumulates its current row group in
+// registers and, when the row group changes, folds the 16 slots (two
+// row-shift adds, then two cross-row shuffles) and stores one partial per
+// weight row.  At the end every output sums the waves' partials in order.
 
 constexpr int kSetBlocks = 16;
 constexpr int kSetK = kSetBlocks * kQK;                   // 512
@@ -387,12 +389,12 @@ __host__ __device__ inline BalLds bal_lds(int m, int64_t k, int rg, int nw, int 
   L.x_bytes = L.x_ops * nw * kWave * 16;
   L.ring_off = L.x_bytes;
   L.part_off = L.ring_off + static_cast<int64_t>(nw) * p * kTaskBytes;
-  // [row group][wave][lane row R][column j] float4 (zero where untouched)
-  L.total = L.part_off + static_cast<int64_t>(rg) * nw * 16 * 16;
+  // [row group][wave][column j] float4 (zero where untouched)
+  L.total = L.part_off + static_cast<int64_t>(rg) * nw * 4 * 16;
   return L;
 }
 
-template <int NW, int P>
+template <int NW, int P, int MR>
 __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, void* __restrict__ y,
     int m, int64_t n, int64_t k, int rows_per_wg, int y_f16) {
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
   uint8_t* const xs = bal_smem;
   uint8_t* const ring = bal_smem + L.ring_off + static_cast<int64_t>(wave) * P * kTaskBytes;
   float4_t* const part = reinterpret_cast<float4_t*>(bal_smem + L.part_off);
-  for (int i = threadIdx.x; i < RG * NW * 16; i += NW * kWave) part[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = threadIdx.x; i < RG * NW * 4; i += NW * kWave) part[i] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   // x staging: wave w copies pieces (w * x_ops + q) * 64 + lane; pieces past
   // the end re-read the last piece into the padding of the region.
@@ -431,17 +433,22 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
   // lanes 0..7) of the 4 x 18 pieces; piece p is row p / 18, column p % 18.
   const int pj0 = lane / 18, pc0 = lane - 18 * (lane / 18);
   const int pj1 = (kWave + lane) / 18, pc1 = (kWave + lane) - 18 * ((kWave + lane) / 18);
-  auto issue_task = [&](int st, int rg, int slot) {
+  // Sources of the lane's two pieces in set 0 of row group rg (rows past n
+  // re-read row n - 1: a ragged last group is computed, never stored).
+  const uint8_t* src0 = W;
+  const uint8_t* src1 = W;
+  auto set_rows = [&](int rg) {
+    int64_t row0 = r0 + 4 * rg + pj0, row1 = r0 + 4 * rg + pj1;
+    if (row0 > n - 1) row0 = n - 1;
+    if (row1 > n - 1) row1 = n - 1;
+    src0 = W + row0 * rb + 16 * pc0;
+    src1 = W + row1 * rb + 16 * pc1;
+  };
+  auto issue_task = [&](int st, int slot) {
     uint8_t* dst = ring + slot * kTaskBytes;
     const int64_t base = static_cast<int64_t>(st) * kTaskRowBytes;
-    int64_t row0 = r0 + 4 * rg + pj0;
-    if (row0 > n - 1) row0 = n - 1;  // ragged last group: computed, never stored
-    dma16(W + row0 * rb + base + 16 * pc0, dst);
-    if (lane < kTaskPieces - kWave) {
-      int64_t row1 = r0 + 4 * rg + pj1;
-      if (row1 > n - 1) row1 = n - 1;
-      dma16(W + row1 * rb + base + 16 * pc1, dst + kWave * 16);
-    }
+    dma16(src0 + base, dst);
+    if (lane < kTaskPieces - kWave) dma16(src1 + base, dst + kWave * 16);
   };
 
   const int j = lane & 3;    // B/D column: weight row within the group; A row
@@ -501,7 +508,8 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
     dword(IC<1>{}, w2, w1);
     dword(IC<2>{}, w3, w2);
     dword(IC<3>{}, w4, w3);
-    accr = d * D + accr;
+#pragma unroll
+    for (int i = 0; i < MR; ++i) accr[i] = d * D[i] + accr[i];
   };
 
   // Fold of the 16 slots per row of 16 lanes: after two row-shift adds lane
@@ -510,9 +518,9 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
   // vector element expression has been compiled as a read of element 0.)
   auto dpp_add = [](float4_t v, auto ctrl) {
     constexpr int c = decltype(ctrl)::value;
-    float4_t r;
+    float4_t r = v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < MR; ++e) {
       const float ve = v[e];
       const int sh = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ve), c, 0xF, 0xF, true);
       r[e] = ve + __builtin_bit_cast(float, sh);
@@ -522,54 +530,64 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
   auto flush = [&](int rg) {
     float4_t v = dpp_add(accr, IC<0x118>{});  // row_shr:8
     v = dpp_add(v, IC<0x114>{});               // row_shr:4
-    if ((lane & 15) >= 12) part[((rg * NW + wave) * 4 + (lane >> 4)) * 4 + (lane & 3)] = v;
+    // ... then the four rows of lanes: (R0 + R1) + (R2 + R3) into row 0.
+#pragma unroll
+    for (int e = 0; e < MR; ++e) {
+      const float ve = v[e];
+      const float a = ve + __shfl_xor(ve, 16);
+      v[e] = a + __shfl_xor(a, 32);
+    }
+    if (lane >= 12 && lane < 16) part[(rg * NW + wave) * 4 + (lane & 3)] = v;
     accr = float4_t{0.f, 0.f, 0.f, 0.f};
   };
 
+  static_assert((P & (P - 1)) == 0, "ring size must be a power of two");
   if (t0 < t1) {
-    int lrg = t0 / S, lset = t0 - (t0 / S) * S, lt = t0;
-    auto next_copy = [&](int slot) {
-      issue_task(lset, lrg, slot);
-      if (lt < t1 - 1) {
-        ++lt;
-        if (++lset == S) { lset = 0; ++lrg; }
+    const int ntask = t1 - t0;
+    int lrg = t0 / S, lset = t0 - (t0 / S) * S, issued = 0;
+    set_rows(lrg);
+    auto next_copy = [&]() {  // task `issued` of this wave into slot issued % P
+      issue_task(lset, issued & (P - 1));
+      ++issued;
+      if (++lset == S) {
+        lset = 0;
+        set_rows(++lrg);
       }
     };
-#pragma unroll
-    for (int i = 0; i < P; ++i) next_copy(i);
-    // This wave's x copies and partial-sum zeroing are complete; the barrier
-    // extends that to every wave.
-    wait_vm_lgkm0<2 * P>();
+    const int npro = ntask < P ? ntask : P;
+    for (int i = 0; i < npro; ++i) next_copy();
+    // This wave's x copies (issued before its 2 npro task copies) and its
+    // partial-sum zeroing are complete; the barrier extends that to every wave.
+    wait_vm_lgkm0_upto<2 * P>(2 * npro);
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     int cset = t0 - (t0 / S) * S, crg = t0 / S;
-    auto task = [&](int i) {
-      wait_vm<2 * (P - 1)>();
-      compiler_fence();
-      compute(ring + i * kTaskBytes, cset);
-      compiler_fence();  // the slot's reads are consumed above
-      next_copy(i);
+    auto finish = [&](int t) {
+      compute(ring + (t & (P - 1)) * kTaskBytes, cset);
       if (++cset == S) {  // row group complete
         cset = 0;
         flush(crg);
         ++crg;
       }
     };
-    // Whole rounds of P tasks (no exit inside a round), then the tail.
-    const int ntask = t1 - t0;
-    int done = 0;
-    for (; done + P <= ntask; done += P) {
-#pragma unroll
-      for (int i = 0; i < P; ++i) task(i);
+    // Steady state: task t has landed when at most 2 (P - 1) copies are in
+    // flight; its slot is then refilled with task t + P.
+    int t = 0;
+    for (; t + P < ntask; ++t) {
+      wait_vm<2 * (P - 1)>();
+      compiler_fence();
+      finish(t);
+      compiler_fence();  // the slot's reads are consumed above
+      next_copy();
     }
-    const int rem = ntask - done;
-#pragma unroll
-    for (int i = 0; i < P - 1; ++i) {
-      if (i >= rem) break;
-      task(i);
+    // The last r <= P tasks are all in flight; nothing more is copied.
+    const int r = ntask - t;
+    for (int q = 0; q < r; ++q) {
+      wait_vm_upto<2 * (P - 1)>(2 * (r - 1 - q));
+      compiler_fence();
+      finish(t + q);
     }
     if (cset != 0) flush(crg);  // the last row group was only partly this wave's
-    wait_vm<0>();  // drain the copies past the last task
   } else {
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();  // matches the barrier of the waves with tasks
@@ -581,12 +599,10 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
   for (int o = threadIdx.x; o < O; o += NW * kWave) {
     const int rl = o / m, mo = o - (o / m) * m;
     const int rg = rl >> 2, jj = rl & 3;
-    const float* q = pf + static_cast<int64_t>(rg) * NW * 64 + jj * 4 + mo;
+    const float* q = pf + static_cast<int64_t>(rg) * NW * 16 + jj * 4 + mo;
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-      for (int R = 0; R < 4; ++R) sum += q[(w * 4 + R) * 16];
+    for (int w = 0; w < NW; ++w) sum += q[w * 16];
     const int64_t off = static_cast<int64_t>(mo) * n + r0 + rl;
     if (y_f16) static_cast<half_t*>(y)[off] = static_cast<half_t>(sum);
     else static_cast<float*>(y)[off] = sum;
@@ -624,7 +640,7 @@ bool bal_plan(int m, int64_t n, int64_t k, BalPlan* p) {
   p->rows_per_wg = static_cast<int>(rows);
   p->grid = static_cast<int>((n + rows - 1) / rows);
   const int rg = static_cast<int>(rows / 4);
-  for (int nw : {16, 8}) {
+  for (int nw : {8, 16}) {
     const BalLds L = bal_lds(m, k, rg, nw, kBalP);
     if (L.total <= kLdsMax) {
       p->nw = nw;
@@ -635,10 +651,10 @@ bool bal_plan(int m, int64_t n, int64_t k, BalPlan* p) {
   return false;
 }
 
-template <int NW>
+template <int NW, int MR>
 hipError_t launch_bal_t(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
                         int64_t n, int64_t k, const BalPlan& p, hipStream_t s) {
-  const void* fn = reinterpret_cast<const void*>(&gemv_bal_kernel<NW, kBalP>);
+  const void* fn = reinterpret_cast<const void*>(&gemv_bal_kernel<NW, kBalP, MR>);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -653,10 +669,19 @@ hipError_t launch_bal_t(const void* x, const uint8_t* packed, void* y, bool y_f1
                          static_cast<size_t>(p.lds), s);
 }
 
+template <int MR>
+hipError_t dispatch_bal_m(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
+                          int64_t n, int64_t k, const BalPlan& p, hipStream_t s) {
+  if (p.nw == 16) return launch_bal_t<16, MR>(x, packed, y, y_f16, m, n, k, p, s);
+  return launch_bal_t<8, MR>(x, packed, y, y_f16, m, n, k, p, s);
+}
+
+// MR: activation rows accumulated (m rounded up to 1, 2 or 4).
 hipError_t dispatch_bal(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
                         int64_t n, int64_t k, const BalPlan& p, hipStream_t s) {
-  if (p.nw == 16) return launch_bal_t<16>(x, packed, y, y_f16, m, n, k, p, s);
-  return launch_bal_t<8>(x, packed, y, y_f16, m, n, k, p, s);
+  if (m == 1) return dispatch_bal_m<1>(x, packed, y, y_f16, m, n, k, p, s);
+  if (m == 2) return dispatch_bal_m<2>(x, packed, y, y_f16, m, n, k, p, s);
+  return dispatch_bal_m<4>(x, packed, y, y_f16, m, n, k, p, s);
 }
 
 }  // namespace
