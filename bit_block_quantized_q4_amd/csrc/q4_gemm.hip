@@ -29,6 +29,11 @@
 namespace q4 {
 namespace {
 
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
 constexpr int BM = 128;       // rows of x per workgroup
 constexpr int BN = 128;       // output features per workgroup
 constexpr int BK = kQK;       // one Q4_0 block per k step
@@ -288,38 +293,61 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
   const int brow = wn * WN + (lane & 31);
   const int kg = lane >> 5;
 
+  // Operand fragments of k16 sub-step kk of a stage (lane: row arow / brow,
+  // 8 k-values 8 kg .. 8 kg + 7 of the sub-step).
+  auto read_frags = [&](const uint8_t* as, int kk, half8_t (&af)[TM], half8_t (&bf)[TN]) {
+    const uint8_t* bs = as + A_STAGE;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      af[i] = *reinterpret_cast<const half8_t*>(as + swz(arow + 32 * i, 2 * kk + kg) * 16);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bf[j] = *reinterpret_cast<const half8_t*>(bs + swz(brow + 32 * j, 2 * kk + kg) * 16);
+  };
+  // Interleave the matrix products of a sub-step with the next sub-step's
+  // operand reads and the dequantisation (one MFMA, one LDS read, two VALU).
+  auto interleave = [](auto with_reads) {
+    constexpr bool R = decltype(with_reads)::value;
+#pragma unroll
+    for (int i = 0; i < TM * TN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (R && i < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+    }
+  };
+
+  half8_t af[2][TM], bf[2][TN];
+  read_frags(smem, 0, af[0], bf[0]);
   for (int ks = 0; ks < nks; ++ks) {
     const int st = ks & 1;
-    const bool more = ks + 1 < nks;
-    if (more) issue_a(ks + 1, st ^ 1);
+    // Activations of step ks + 1 into the other stage (the last step copies
+    // its own again: that stage is no longer read).
+    issue_a(ks + 1 < nks ? ks + 1 : ks, st ^ 1);
     const Units cur = nxt;
     nxt = load_units(ks + 2 < nks ? ks + 2 : nks - 1);
     const uint8_t* as = smem + st * STAGE;
-    const uint8_t* bs = as + A_STAGE;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {  // 16-wide k sub-steps
-      half8_t af[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(as + swz(arow + 32 * i, 2 * kk + kg) * 16);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bf[j] = *reinterpret_cast<const half8_t*>(bs + swz(brow + 32 * j, 2 * kk + kg) * 16);
+      const int c = kk & 1;
+      if (kk < 3) read_frags(as, kk + 1, af[c ^ 1], bf[c ^ 1]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      // Interleave the next step's dequantisation with the products.
-      if (more) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
+      // The next step's weights (on the last step: a harmless rewrite of the
+      // stage no longer read).
 #pragma unroll
-        for (int u = 0; u < UNITS; ++u)
-          if (u % 4 == kk) dequant_store(cur.v[u], u, st ^ 1);
-      }
+      for (int u = 0; u < UNITS; ++u)
+        if (u % 4 == kk) dequant_store(cur.v[u], u, st ^ 1);
+      if (kk < 3) interleave(IC<true>{});
+      else interleave(IC<false>{});
+      __builtin_amdgcn_sched_barrier(0);
     }
     wait_vm<0>();
     tie_units(nxt);
     __syncthreads();
+    read_frags(smem + (st ^ 1) * STAGE, 0, af[0], bf[0]);
   }
 
   // 32x32 accumulator layout: lane l holds column l % 32; register r holds
