@@ -152,35 +152,36 @@ struct WUnit {
   uint32_t d;  // fp16 scale in the low half
 };
 
-template <int BM, int BN, typename YT>
-__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
+template <int BM, int BN, int WVM, int WVN, typename YT>
+__global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, YT* __restrict__ y,
     int64_t m, int64_t n, int64_t k) {
-  constexpr int WM = BM / 2, WN = BN / 2;   // wave tile
+  constexpr int NTH = WVM * WVN * 64;       // threads
+  constexpr int WM = BM / WVM, WN = BN / WVN;  // wave tile
   constexpr int TM = WM / 32, TN = WN / 32; // 32 x 32 products per wave
   constexpr int A_STAGE = BM * kRowBytes16;
   constexpr int B_STAGE = BN * kRowBytes16;
   constexpr int STAGE = A_STAGE + B_STAGE;
-  constexpr int A_COPIES = BM * 8 / 256;    // 16-byte copies per thread per step
-  constexpr int UNITS = BN * 4 / 256;       // weight units per thread per step
+  constexpr int A_COPIES = BM * 8 / NTH;    // 16-byte copies per thread per step
+  constexpr int UNITS = BN * 4 / NTH;       // weight units per thread per step
   static_assert(A_COPIES >= 1 && UNITS >= 1, "tile too small");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WVN, wn = wave % WVN;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
   const int64_t rb = (k / kQK) * kBlockBytes;
   const int nks = static_cast<int>(k / kBK);
 
-  // Activation copies: copy i of this thread is LDS piece P = 256 i + tid
+  // Activation copies: copy i of this thread is LDS piece P = NTH i + tid
   // (row P / 8, swizzled column P % 8); the source column undoes the swizzle.
   const half_t* asrc[A_COPIES];
 #pragma unroll
   for (int i = 0; i < A_COPIES; ++i) {
-    const int P = 256 * i + tid;
+    const int P = NTH * i + tid;
     const int r = P >> 3;
     const int c = (P & 7) ^ (r & 7);
     const int64_t row = m0 + r < m ? m0 + r : m - 1;
@@ -190,10 +191,10 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
     uint8_t* dst = smem + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < A_COPIES; ++i)
-      dma16(asrc[i] + static_cast<int64_t>(ks) * kBK, dst + (256 * i + 64 * wave) * 16);
+      dma16(asrc[i] + static_cast<int64_t>(ks) * kBK, dst + (NTH * i + 64 * wave) * 16);
   };
 
-  // Weight units: unit u of this thread is U = 256 u + tid: row U / 4,
+  // Weight units: unit u of this thread is U = NTH u + tid: row U / 4,
   // block (U / 2) % 2 of the step, half U % 2 (code bytes 8h .. 8h+7).
   const uint8_t* wsrc[UNITS];
   const uint16_t* dsrc[UNITS];
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
   int wrow[UNITS], wpiece_lo[UNITS];
 #pragma unroll
   for (int u = 0; u < UNITS; ++u) {
-    const int U = 256 * u + tid;
+    const int U = NTH * u + tid;
     const int r = U >> 2;
     const int b = (U >> 1) & 1;
     const int h = U & 1;
@@ -364,21 +365,21 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(
       }
 }
 
-template <int BM, int BN, typename YT>
+template <int BM, int BN, int WVM, int WVN, typename YT>
 hipError_t launch_tiled(const half_t* x, const uint8_t* packed, YT* y, int64_t m, int64_t n,
                         int64_t k, hipStream_t s) {
   void* argv[] = {const_cast<const half_t**>(&x), const_cast<const uint8_t**>(&packed), &y, &m,
                   &n, &k};
   const dim3 grid(static_cast<unsigned>((n + BN - 1) / BN), static_cast<unsigned>((m + BM - 1) / BM));
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, YT>), grid,
-                         dim3(256), argv, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, WVM, WVN, YT>),
+                         grid, dim3(WVM * WVN * 64), argv, 0, s);
 }
 
 template <typename YT>
 hipError_t dispatch_tiled(const half_t* x, const uint8_t* packed, YT* y, int64_t m, int64_t n,
                           int64_t k, hipStream_t s) {
-  if (m >= 1024) return launch_tiled<256, 256, YT>(x, packed, y, m, n, k, s);
-  return launch_tiled<128, 128, YT>(x, packed, y, m, n, k, s);
+  if (m >= 1024) return launch_tiled<256, 256, 2, 4, YT>(x, packed, y, m, n, k, s);
+  return launch_tiled<128, 128, 2, 2, YT>(x, packed, y, m, n, k, s);
 }
 
 }  // namespace
