@@ -41,6 +41,7 @@ COMMON_FLAGS = [
 # its large accumulators in AGPRs (the default form).
 PER_FILE_FLAGS = {
     "q4_gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "q4_gemv_tile.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -485,7 +485,6 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
     // A operand of (u, h): activation dwords 8h + 2u and 8h + 2u + 1.
     auto a_op = [&](auto uu, auto hh) {
       constexpr int dw = 8 * decltype(hh)::value + 2 * decltype(uu)::value;
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       const u32x2 pr = {xr[dw >> 2][dw & 3], xr[dw >> 2][(dw & 3) + 1]};
       return __builtin_bit_cast(half4_t, pr);
     };
@@ -612,18 +611,6 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
 constexpr int64_t kLdsMax = 160 * 1024;
 constexpr int kBalP = 4;  // tasks in flight per wave
 
-int device_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
 
 struct BalPlan {
   int rows_per_wg = 0, grid = 0, nw = 0;
@@ -686,11 +673,26 @@ hipError_t dispatch_bal(const void* x, const uint8_t* packed, void* y, bool y_f1
 
 }  // namespace
 
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_gemv(const void* x, DType xt, const uint8_t* packed, void* y,
                        DType yt, int m, int64_t n, int64_t k, hipStream_t s) {
   BalPlan plan;
   if (xt == DType::F16 && bal_plan(m, n, k, &plan))
     return dispatch_bal(x, packed, y, yt == DType::F16, m, n, k, plan, s);
+  if (xt == DType::F16 && gemv_tile_supports(m, k))
+    return launch_gemv_tile(x, packed, y, yt == DType::F16, m, n, k, s);
   if (xt == DType::F16 && stream_supports(k))
     return dispatch_stream(x, packed, y, yt == DType::F16, m, n, k, s);
   if (xt == DType::F16) {

@@ -1,0 +1,354 @@
+// Q4_0 decode GEMV on 16 x 16 x 32 matrix cores: y[i, r] = sum_j x[i, j] w[r, j]
+// for a batch of up to 32 activation rows (llama.cpp's Q4_0 block page, block
+// layout; the serving page's batched decode step).
+//
+// One workgroup owns 16 T consecutive weight rows over the whole of K, so no
+// partial sums leave the workgroup.  K is walked in phases of PB blocks
+// (32 PB weights).  For every phase the eight waves copy, global -> LDS, the
+// phase's weight bytes of the 16 T rows and the phase's activation columns
+// (16-byte copies); three phases are resident in a ring, so the
+// copies of phase p + 2 are in flight while phase p is computed.  Within a
+// phase wave w owns blocks w PB / 8 .. (w + 1) PB / 8 - 1 for all 16 T rows;
+// each (row tile, block) pair is one v_mfma_f32_16x16x32_f16 with 16
+// activation rows on the A side and 16 weight rows on the B side.  The block's
+// 32 codes enter as fp16 subnormals q 2^-24 (the nibble is the whole
+// mantissa), and the matrix core's accumulator input carries the code offset,
+// -8 2^-24 sum(x), which one extra product of the activations with a
+// constant gives once per block for all row tiles; the block scale d is then
+// applied in fp32 to the 4 outputs the lane holds (lane l: weight row l % 16,
+// activation rows 4 (l / 16) .. +3) and the sums are rescaled by 2^24 at the
+// end.
+//
+// Bank layout: a weight row occupies an odd number of 16-byte pieces (the
+// phase's 9 PB / 8 data pieces plus one padding piece), so the 16 rows one
+// column read touches fall in 8 distinct bank quads (2-way at most); an
+// activation row's 16-byte pieces are stored XOR-swizzled by the row index,
+// so the 16 rows one operand read touches spread over all banks.
+#include "q4_device.hpp"
+
+namespace q4 {
+namespace {
+
+constexpr int kTSlots = 3;   // phases resident in LDS
+
+template <int V>
+struct TC {
+  static constexpr int value = V;
+};
+
+// Unrolled loop over a compile-time range: f(TC<0>{}), ..., f(TC<N - 1>{}).
+template <int I, int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  if constexpr (I < N) {
+    f(TC<I>{});
+    unroll<I + 1, N>(f);
+  }
+}
+
+// Geometry of one phase slot for T row tiles, AT activation tiles, PB blocks
+// per phase and NW waves.
+template <int T, int AT, int PB, int NW>
+struct TileGeo {
+  static constexpr int nw = NW;
+  static constexpr int lanes = NW * kWave;
+  static constexpr int jb = PB / NW;                      // blocks per wave per phase
+  static constexpr int row_pc = PB * kBlockBytes / 16;    // weight pieces per row
+  static constexpr int wstride_pc = row_pc + 1;           // odd row stride (pieces)
+  static constexpr int wstride = 16 * wstride_pc;
+  static constexpr int wpos = 16 * T * wstride_pc;        // weight pieces per slot
+  static constexpr int niw = (wpos + lanes - 1) / lanes;  // copy rounds (max per wave)
+  static constexpr int wbytes = (16 * wpos + 255) / 256 * 256;
+  static constexpr int xp = PB * kQK * 2 / 16;            // 16-byte pieces per activation row
+  static constexpr int nix_max = (16 * AT * xp + lanes - 1) / lanes;
+  static constexpr int xbytes = 16 * AT * xp * 16;
+  static constexpr int slot = wbytes + xbytes;
+  static constexpr int red = T * AT * NW * kWave * 16;
+  static constexpr int lds = kTSlots * slot > red ? kTSlots * slot : red;
+  static constexpr int phase_k = PB * kQK;
+  static constexpr int ndma = niw + nix_max;              // copy instructions per phase (max)
+  static constexpr int tiles = T * jb;                    // (row tile, block) pairs per wave
+  static constexpr int dma_per_tile = (ndma + tiles - 1) / tiles;
+  static_assert(PB % (2 * NW) == 0, "blocks per wave must be even");
+  static_assert((PB * kBlockBytes) % 16 == 0, "row segments of whole pieces");
+  static_assert(xp >= 16, "swizzle needs 16 pieces per row");
+};
+
+template <int T, int AT, int PB, int NW>
+__global__ __launch_bounds__(NW * kWave, 1) void gemv_tile_kernel(
+    const half_t* __restrict__ x, const uint8_t* __restrict__ W, void* __restrict__ y, int m,
+    int64_t n, int64_t k, int y_f16) {
+  using G = TileGeo<T, AT, PB, NW>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * (16 * T);
+  const int64_t rb = (k / kQK) * kBlockBytes;  // bytes per weight row
+  const int nph = static_cast<int>(k / G::phase_k);
+  const uint32_t smem = lds_addr(tsm);
+
+  // Weight copies.  Slot piece i = (q NW + wave) 64 + lane holds piece
+  // i % wstride_pc of the phase's segment of row i / wstride_pc (the padding
+  // piece repeats the last one; rows past n read row n - 1, computed and
+  // never stored).  Lanes past the slot's pieces copy nothing; a wave issues
+  // the rounds q in which any of its lanes copies (cw of them).
+  uint32_t wsrc[G::niw];
+#pragma unroll
+  for (int q = 0; q < G::niw; ++q) {
+    int i = (q * NW + wave) * kWave + lane;
+    if (i > G::wpos - 1) i = G::wpos - 1;
+    const int r = i / G::wstride_pc;
+    int c = i - r * G::wstride_pc;
+    if (c > G::row_pc - 1) c = G::row_pc - 1;
+    int64_t grow = row0 + r;
+    if (grow > n - 1) grow = n - 1;
+    wsrc[q] = static_cast<uint32_t>((grow - row0) * rb + 16 * c);
+  }
+  int cw = 0;
+#pragma unroll
+  for (int q = 0; q < G::niw; ++q) cw += ((q * NW + wave) * kWave < G::wpos) ? 1 : 0;
+  // Activation copies: piece position i of the slot's activation area holds
+  // piece (i % xp) ^ (row & 15) of row i / xp of the phase's columns; only
+  // the m real rows are copied (a wave issues the cx rounds in which any of
+  // its lanes copies).
+  const int xpos = m * G::xp;
+  int cx = 0;
+#pragma unroll
+  for (int q = 0; q < G::nix_max; ++q) cx += ((q * NW + wave) * kWave < xpos) ? 1 : 0;
+  uint32_t xsrc[G::nix_max];
+#pragma unroll
+  for (int q = 0; q < G::nix_max; ++q) {
+    int i = (q * NW + wave) * kWave + lane;
+    if (i > xpos - 1) i = xpos - 1;
+    const int ar = i / G::xp;
+    const int pc = (i - ar * G::xp) ^ (ar & 15);
+    xsrc[q] = static_cast<uint32_t>((static_cast<int64_t>(ar) * k + 8 * pc) * 2);
+  }
+  const uint8_t* const wbase = W + row0 * rb;
+  const uint8_t* const xbase = reinterpret_cast<const uint8_t*>(x);
+
+  // Copy instruction c (0 .. ndma - 1) of phase p: weight rounds first, then
+  // activation rounds; a round with no copying lane is not issued.
+  auto issue_one = [&](auto cc, int p) {
+    constexpr int c = decltype(cc)::value;
+    const uint32_t sb = smem + (p % kTSlots) * G::slot;
+    if constexpr (c < G::niw) {
+      const int i0 = (c * NW + wave) * kWave;
+      const uint8_t* ws = wbase + static_cast<int64_t>(p) * (PB * kBlockBytes);
+      if (i0 < G::wpos && i0 + lane < G::wpos) dma16_sbase(wsrc[c], ws, sb + i0 * 16);
+    } else {
+      constexpr int q = c - G::niw;
+      const int i0 = (q * NW + wave) * kWave;
+      const uint8_t* xs = xbase + static_cast<int64_t>(p) * (G::phase_k * 2);
+      if (i0 < xpos && i0 + lane < xpos) dma16_sbase(xsrc[q], xs, sb + G::wbytes + i0 * 16);
+    }
+  };
+  auto issue = [&](int p) { unroll<0, G::ndma>([&](auto cc) { issue_one(cc, p); }); };
+
+  // Lane roles: B side weight row r = lane % 16 and code dword g = lane / 16;
+  // A side activation row a = lane % 16 (rows past m read row m - 1) and the
+  // same g.  Byte offsets within a slot.
+  const int r = lane & 15, g = lane >> 4;
+  const uint32_t rs0 = r * G::wstride + wave * (G::jb * kBlockBytes);  // scale of block 0
+  const uint32_t rg0 = rs0 + 4 * g;                                     // code dword g
+  uint32_t xa[G::jb][2][AT];  // activation operand halves (elements 4g.. and 16 + 4g..)
+#pragma unroll
+  for (int t = 0; t < AT; ++t) {
+    int ar = r + 16 * t;
+    if (ar > m - 1) ar = m - 1;
+    const int sw = ar & 15;
+#pragma unroll
+    for (int j = 0; j < G::jb; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int pc = 4 * (wave * G::jb + j) + 2 * h + (g >> 1);
+        xa[j][h][t] = G::wbytes + ar * (G::xp * 16) + 16 * (pc ^ sw) + 8 * (g & 1);
+      }
+  }
+  float4_t acc[T][AT];
+#pragma unroll
+  for (int i = 0; i < T; ++i)
+#pragma unroll
+    for (int t = 0; t < AT; ++t) acc[i][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int p, int pi) {
+    const uint8_t* slot = tsm + (p % kTSlots) * G::slot;
+    half8_t A[G::jb][AT];
+#pragma unroll
+    for (int j = 0; j < G::jb; ++j)
+#pragma unroll
+      for (int t = 0; t < AT; ++t) {
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(slot + xa[j][0][t]);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(slot + xa[j][1][t]);
+        A[j][t] = __builtin_bit_cast(half8_t, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
+    // Code offset of block j: -8 2^-24 sum over the block of x, per activation
+    // row, in the output layout (a product with a constant -2^-21 operand).
+    const half8_t kneg = {static_cast<half_t>(-0x1p-21f), static_cast<half_t>(-0x1p-21f),
+                          static_cast<half_t>(-0x1p-21f), static_cast<half_t>(-0x1p-21f),
+                          static_cast<half_t>(-0x1p-21f), static_cast<half_t>(-0x1p-21f),
+                          static_cast<half_t>(-0x1p-21f), static_cast<half_t>(-0x1p-21f)};
+    float4_t C[G::jb][AT];
+#pragma unroll
+    for (int j = 0; j < G::jb; ++j)
+#pragma unroll
+      for (int t = 0; t < AT; ++t)
+        C[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j][t], kneg, float4_t{0.f, 0.f, 0.f, 0.f},
+                                                         0, 0, 0);
+    unroll<0, T>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      constexpr int rt = i * 16 * G::wstride;
+      unroll<0, G::jb>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        constexpr int bo = rt + j * kBlockBytes;
+        // this tile's share of the copies of phase pi
+        if (pi >= 0) {
+          unroll<0, G::dma_per_tile>([&](auto kk) {
+            constexpr int c = (i * G::jb + j) * G::dma_per_tile + decltype(kk)::value;
+            if constexpr (c < G::ndma) issue_one(TC<c>{}, pi);
+          });
+        }
+        const float d = half_bits_to_float(*reinterpret_cast<const uint16_t*>(slot + rs0 + bo));
+        half8_t bw;
+        if constexpr ((j & 1) == 0) {
+          // even block: code bytes 4g .. 4g+3 are bytes 2..5 of the window at 4g
+          const uint32_t w0 = *reinterpret_cast<const uint32_t*>(slot + rg0 + bo);
+          const uint32_t w1 = *reinterpret_cast<const uint32_t*>(slot + rg0 + bo + 4);
+          bw = unpack8_sub<2>(w0, w1);
+        } else {
+          // odd block: they are the aligned dword at 4g + 2
+          const uint32_t c = *reinterpret_cast<const uint32_t*>(slot + rg0 + bo + 2);
+          bw = unpack8_sub<0>(c, c);
+        }
+#pragma unroll
+        for (int t = 0; t < AT; ++t) {
+          const float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j][t], bw, C[j][t], 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][t][e] = d * D[e] + acc[i][t][e];
+        }
+      });
+    });
+  };
+
+  // Phase p: once only phase p + 1's copies are in flight (none when p is the
+  // last phase) this wave's copies of p have landed; the barrier extends that
+  // to every wave and frees the slot of phase p - 1, which phase p + 2's
+  // copies then reuse.
+  constexpr int kMaxInFlight = G::niw + G::nix_max;
+  const int per_phase = cw + cx;
+  issue(0);
+  if (nph > 1) issue(1);
+  for (int p = 0; p < nph; ++p) {
+    wait_vm_upto<kMaxInFlight>(p + 1 < nph ? per_phase : 0);
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    compute(p, p + 2 < nph ? p + 2 : -1);
+    compiler_fence();
+  }
+
+  // Sum the eight waves' partial tiles (the ring is free once every wave has
+  // passed this barrier).
+  __syncthreads();
+  float4_t* red = reinterpret_cast<float4_t*>(tsm);
+#pragma unroll
+  for (int i = 0; i < T; ++i)
+#pragma unroll
+    for (int t = 0; t < AT; ++t) red[((i * AT + t) * NW + wave) * kWave + lane] = acc[i][t];
+  __syncthreads();
+  const float* rf = reinterpret_cast<const float*>(tsm);
+  const int O = T * 16 * m;
+  for (int o = threadIdx.x; o < O; o += G::lanes) {
+    const int i = o / (16 * m);
+    const int rem = o - i * 16 * m;
+    const int ar = rem >> 4, wr = rem & 15;
+    const int t = ar >> 4, aa = ar & 15;
+    const int l = wr + 16 * (aa >> 2), e = aa & 3;
+    const float* q = rf + (static_cast<int64_t>((i * AT + t) * NW) * kWave + l) * 4 + e;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += q[w * kWave * 4];
+    sum *= 0x1p24f;  // exact rescale of the subnormal code products
+    const int64_t row = row0 + 16 * i + wr;
+    if (row < n) {
+      const int64_t off = static_cast<int64_t>(ar) * n + row;
+      if (y_f16) static_cast<half_t*>(y)[off] = static_cast<half_t>(sum);
+      else static_cast<float*>(y)[off] = sum;
+    }
+  }
+}
+
+constexpr int kTLdsMax = 160 * 1024;
+
+template <int T, int AT, int PB, int NW = (PB == 32 ? 16 : 8)>
+hipError_t launch_tile_t(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
+                         int64_t n, int64_t k, hipStream_t s) {
+  using G = TileGeo<T, AT, PB, NW>;
+  static_assert(G::lds <= kTLdsMax, "LDS budget");
+  const void* fn = reinterpret_cast<const void*>(&gemv_tile_kernel<T, AT, PB, NW>);
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
+    const hipError_t e =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kTLdsMax);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t grid = (n + 16 * T - 1) / (16 * T);
+  const half_t* xp = static_cast<const half_t*>(x);
+  int yf = y_f16 ? 1 : 0;
+  void* argv[] = {&xp, const_cast<const uint8_t**>(&packed), &y, &m, &n, &k, &yf};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(G::lanes), argv,
+                         static_cast<size_t>(G::lds), s);
+}
+
+struct TilePlan {
+  int T, AT, PB;
+};
+
+// Row tiles per workgroup: enough for one workgroup per compute unit, capped
+// where the LDS ring would not fit (larger matrices take several rounds).
+TilePlan tile_plan(int m, int64_t n, int64_t k) {
+  const int64_t tiles = (n + 15) / 16;
+  const int64_t cu = device_cu_count();
+  int64_t t = (tiles + cu - 1) / cu;
+  if (t < 1) t = 1;
+  TilePlan p;
+  p.AT = m > 16 ? 2 : 1;
+  if (p.AT == 1 && t <= 2 && k % 1024 == 0) {
+    p.T = static_cast<int>(t);
+    p.PB = 32;
+  } else {
+    p.T = static_cast<int>(t > (p.AT == 1 ? 5 : 4) ? (p.AT == 1 ? 5 : 4) : t);
+    p.PB = 16;
+  }
+  return p;
+}
+
+template <int AT, int PB>
+hipError_t launch_tile_tt(const TilePlan& p, const void* x, const uint8_t* packed, void* y,
+                          bool y_f16, int m, int64_t n, int64_t k, hipStream_t s) {
+  switch (p.T) {
+    case 1: return launch_tile_t<1, AT, PB>(x, packed, y, y_f16, m, n, k, s);
+    case 2: return launch_tile_t<2, AT, PB>(x, packed, y, y_f16, m, n, k, s);
+    case 3: return launch_tile_t<3, AT, PB>(x, packed, y, y_f16, m, n, k, s);
+    case 4: return launch_tile_t<4, AT, PB>(x, packed, y, y_f16, m, n, k, s);
+    default:
+      if constexpr (AT == 1 && PB == 16) return launch_tile_t<5, AT, PB>(x, packed, y, y_f16, m, n, k, s);
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool gemv_tile_supports(int m, int64_t k) { return m >= 1 && m <= 32 && k > 0 && k % 512 == 0; }
+
+hipError_t launch_gemv_tile(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
+                            int64_t n, int64_t k, hipStream_t s) {
+  const TilePlan p = tile_plan(m, n, k);
+  if (p.AT == 2) return launch_tile_tt<2, 16>(p, x, packed, y, y_f16, m, n, k, s);
+  if (p.PB == 32) {
+    if (p.T == 1) return launch_tile_t<1, 1, 32>(x, packed, y, y_f16, m, n, k, s);
+    return launch_tile_t<2, 1, 32>(x, packed, y, y_f16, m, n, k, s);
+  }
+  return launch_tile_tt<1, 16>(p, x, packed, y, y_f16, m, n, k, s);
+}
+
+}  // namespace q4

@@ -32,6 +32,14 @@ hipError_t launch_quantize(const void* w, DType wt, int64_t n, int64_t k,
 hipError_t launch_gemv(const void* x, DType xt, const uint8_t* packed, void* y,
                        DType yt, int m, int64_t n, int64_t k, hipStream_t s);
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cu_count();
+
+// Decode GEMV on 16x16x32 matrix cores (k a multiple of 1024, m <= 32).
+bool gemv_tile_supports(int m, int64_t k);
+hipError_t launch_gemv_tile(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
+                            int64_t n, int64_t k, hipStream_t s);
+
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm(const void* x, DType xt, const uint8_t* packed, void* y,
                        DType yt, int64_t m, int64_t n, int64_t k,

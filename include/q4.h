@@ -105,8 +105,11 @@ q4_status q4_quantize(const void *w, int w_dtype, int64_t n, int64_t k,
 /* Batched-decode GEMV: y[m][n] = x[m][k] . dequant(packed)^T for
  * 1 <= m <= Q4_GEMV_MAX_M (the page's batched decode stage).  x is Q4_F32 or
  * Q4_F16, y is Q4_F32 or Q4_F16.  Every output is the fp32 sum over blocks of
- * d times the exact block dot product of x with (q - 8), rounded once to the
- * output dtype.  Streams each packed byte from memory once per call. */
+ * d times the block dot product of x with (q - 8), rounded once to the output
+ * dtype.  The block dot products are exact for m <= 4; for larger m with fp16
+ * x and k a multiple of 512 they come from fp16 matrix cores fed the codes as
+ * fp16 subnormals, within about 1e-6 of exact relative to their magnitude
+ * sum.  Streams each packed byte from memory once per call. */
 q4_status q4_gemv(const void *x, int x_dtype, const void *packed, void *y,
                   int y_dtype, int64_t m, int64_t n, int64_t k,
                   q4_stream_t stream);

@@ -174,3 +174,17 @@ def test_row_group_shapes(q4lib, gpu, m, n, k):
     packed = oracle.quantize(w)
     g = run_gemv(q4lib, x, packed, n, k, "f16", gpu)
     assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")
+
+
+@pytest.mark.parametrize("m", [5, 16, 17, 32])
+@pytest.mark.parametrize("n,k", [(16, 3072), (4097, 1536), (4097, 3072), (8200, 1536),
+                                 (12300, 1536), (16400, 512)])
+def test_matrix_core_tile_shapes(q4lib, gpu, m, n, k):
+    """The 16x16x32 matrix-core GEMV (m > 4, k a multiple of 512): one to five
+    16-row tiles per workgroup, one or two activation tiles, one to six K
+    phases, a ragged last row tile."""
+    w = synth.random_weights(11 * m + n + k, n, k, "outlier")
+    x = synth.random_activations(13 * m + k, m, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemv(q4lib, x, packed, n, k, "f16", gpu)
+    assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")

@@ -36,9 +36,12 @@ def asm(src):
 pytestmark = pytest.mark.skipif(not Path(HIPCC).exists(), reason="hipcc not available")
 
 
-@pytest.mark.parametrize("src", ["q4_gemv.hip", "q4_gemm.hip", "q4_quantize.hip"])
+@pytest.mark.parametrize("src", sorted(p.name for p in CSRC.glob("*.hip")))
 def test_no_scratch_or_spills(src):
     meta = metadata(asm(src))
+    if src == "q4_api.hip":  # host code only
+        assert not meta
+        return
     assert meta, "no kernels found"
     for name, m in meta.items():
         assert m["private_segment_fixed_size"] == 0, name
@@ -47,7 +50,8 @@ def test_no_scratch_or_spills(src):
 
 @pytest.mark.parametrize("src,pattern", [("q4_gemm.hip", "gemm_mfma_kernel"),
                                          ("q4_gemv.hip", "gemv_bal_kernel"),
-                                         ("q4_gemv.hip", "gemv_stream_kernel")])
+                                         ("q4_gemv.hip", "gemv_stream_kernel"),
+                                         ("q4_gemv_tile.hip", "gemv_tile_kernel")])
 def test_no_register_used_before_its_load_lands(src, pattern):
     ks = kernels(asm(src), pattern)
     assert ks, pattern
