@@ -46,20 +46,23 @@ __device__ __forceinline__ void unroll(F&& f) {
 }
 
 // Geometry of one phase slot for T row tiles, AT activation tiles, PB blocks
-// per phase and NW waves.
-template <int T, int AT, int PB, int NW>
+// per phase, NW computing waves and NP copying waves (NP = 0: the computing
+// waves copy too).
+template <int T, int AT, int PB, int NW, int NP>
 struct TileGeo {
   static constexpr int nw = NW;
-  static constexpr int lanes = NW * kWave;
+  static constexpr int lanes = (NW + NP) * kWave;         // threads of the workgroup
+  static constexpr int cwaves = NP > 0 ? NP : NW;         // copying waves
+  static constexpr int clanes = cwaves * kWave;
   static constexpr int jb = PB / NW;                      // blocks per wave per phase
   static constexpr int row_pc = PB * kBlockBytes / 16;    // weight pieces per row
   static constexpr int wstride_pc = row_pc + 1;           // odd row stride (pieces)
   static constexpr int wstride = 16 * wstride_pc;
   static constexpr int wpos = 16 * T * wstride_pc;        // weight pieces per slot
-  static constexpr int niw = (wpos + lanes - 1) / lanes;  // copy rounds (max per wave)
+  static constexpr int niw = (wpos + clanes - 1) / clanes;  // copy rounds (max per wave)
   static constexpr int wbytes = (16 * wpos + 255) / 256 * 256;
   static constexpr int xp = PB * kQK * 2 / 16;            // 16-byte pieces per activation row
-  static constexpr int nix_max = (16 * AT * xp + lanes - 1) / lanes;
+  static constexpr int nix_max = (16 * AT * xp + clanes - 1) / clanes;
   static constexpr int xbytes = 16 * AT * xp * 16;
   static constexpr int slot = wbytes + xbytes;
   static constexpr int red = T * AT * NW * kWave * 16;
@@ -73,20 +76,23 @@ struct TileGeo {
   static_assert(xp >= 16, "swizzle needs 16 pieces per row");
 };
 
-template <int T, int AT, int PB, int NW>
-__global__ __launch_bounds__(NW * kWave, 1) void gemv_tile_kernel(
+template <int T, int AT, int PB, int NW, int NP>
+__global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, void* __restrict__ y, int m,
     int64_t n, int64_t k, int y_f16) {
-  using G = TileGeo<T, AT, PB, NW>;
+  using G = TileGeo<T, AT, PB, NW, NP>;
+  constexpr int CW = G::cwaves;
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  // copying-wave index (waves NW .. NW + NP - 1 copy when NP > 0)
+  const int cwave = NP > 0 ? (wave >= NW ? wave - NW : 0) : wave;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * (16 * T);
   const int64_t rb = (k / kQK) * kBlockBytes;  // bytes per weight row
   const int nph = static_cast<int>(k / G::phase_k);
   const uint32_t smem = lds_addr(tsm);
 
-  // Weight copies.  Slot piece i = (q NW + wave) 64 + lane holds piece
+  // Weight copies.  Slot piece i = (q CW + cwave) 64 + lane holds piece
   // i % wstride_pc of the phase's segment of row i / wstride_pc (the padding
   // piece repeats the last one; rows past n read row n - 1, computed and
   // never stored).  Lanes past the slot's pieces copy nothing; a wave issues
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void gemv_tile_kernel(
   uint32_t wsrc[G::niw];
 #pragma unroll
   for (int q = 0; q < G::niw; ++q) {
-    int i = (q * NW + wave) * kWave + lane;
+    int i = (q * CW + cwave) * kWave + lane;
     if (i > G::wpos - 1) i = G::wpos - 1;
     const int r = i / G::wstride_pc;
     int c = i - r * G::wstride_pc;
@@ -105,7 +111,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void gemv_tile_kernel(
   }
   int cw = 0;
 #pragma unroll
-  for (int q = 0; q < G::niw; ++q) cw += ((q * NW + wave) * kWave < G::wpos) ? 1 : 0;
+  for (int q = 0; q < G::niw; ++q) cw += ((q * CW + cwave) * kWave < G::wpos) ? 1 : 0;
   // Activation copies: piece position i of the slot's activation area holds
   // piece (i % xp) ^ (row & 15) of row i / xp of the phase's columns; only
   // the m real rows are copied (a wave issues the cx rounds in which any of
@@ -113,11 +119,11 @@ __global__ __launch_bounds__(NW * kWave, 1) void gemv_tile_kernel(
   const int xpos = m * G::xp;
   int cx = 0;
 #pragma unroll
-  for (int q = 0; q < G::nix_max; ++q) cx += ((q * NW + wave) * kWave < xpos) ? 1 : 0;
+  for (int q = 0; q < G::nix_max; ++q) cx += ((q * CW + cwave) * kWave < xpos) ? 1 : 0;
   uint32_t xsrc[G::nix_max];
 #pragma unroll
   for (int q = 0; q < G::nix_max; ++q) {
-    int i = (q * NW + wave) * kWave + lane;
+    int i = (q * CW + cwave) * kWave + lane;
     if (i > xpos - 1) i = xpos - 1;
     const int ar = i / G::xp;
     const int pc = (i - ar * G::xp) ^ (ar & 15);
@@ -132,12 +138,12 @@ __global__ __launch_bounds__(NW * kWave, 1) void gemv_tile_kernel(
     constexpr int c = decltype(cc)::value;
     const uint32_t sb = smem + (p % kTSlots) * G::slot;
     if constexpr (c < G::niw) {
-      const int i0 = (c * NW + wave) * kWave;
+      const int i0 = (c * CW + cwave) * kWave;
       const uint8_t* ws = wbase + static_cast<int64_t>(p) * (PB * kBlockBytes);
       if (i0 < G::wpos && i0 + lane < G::wpos) dma16_sbase(wsrc[c], ws, sb + i0 * 16);
     } else {
       constexpr int q = c - G::niw;
-      const int i0 = (q * NW + wave) * kWave;
+      const int i0 = (q * CW + cwave) * kWave;
       const uint8_t* xs = xbase + static_cast<int64_t>(p) * (G::phase_k * 2);
       if (i0 < xpos && i0 + lane < xpos) dma16_sbase(xsrc[q], xs, sb + G::wbytes + i0 * 16);
     }
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void gemv_tile_kernel(
         constexpr int j = decltype(jj)::value;
         constexpr int bo = rt + j * kBlockBytes;
         // this tile's share of the copies of phase pi
-        if (pi >= 0) {
+        if (NP == 0 && pi >= 0) {
           unroll<0, G::dma_per_tile>([&](auto kk) {
             constexpr int c = (i * G::jb + j) * G::dma_per_tile + decltype(kk)::value;
             if constexpr (c < G::ndma) issue_one(TC<c>{}, pi);
@@ -230,29 +236,51 @@ __global__ __launch_bounds__(NW * kWave, 1) void gemv_tile_kernel(
   };
 
   // Phase p: once only phase p + 1's copies are in flight (none when p is the
-  // last phase) this wave's copies of p have landed; the barrier extends that
-  // to every wave and frees the slot of phase p - 1, which phase p + 2's
+  // last phase) a copying wave's copies of p have landed; the barrier extends
+  // that to every wave and frees the slot of phase p - 1, which phase p + 2's
   // copies then reuse.
   constexpr int kMaxInFlight = G::niw + G::nix_max;
   const int per_phase = cw + cx;
-  issue(0);
-  if (nph > 1) issue(1);
-  for (int p = 0; p < nph; ++p) {
-    wait_vm_upto<kMaxInFlight>(p + 1 < nph ? per_phase : 0);
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-    compute(p, p + 2 < nph ? p + 2 : -1);
-    compiler_fence();
+  if constexpr (NP == 0) {
+    issue(0);
+    if (nph > 1) issue(1);
+    for (int p = 0; p < nph; ++p) {
+      wait_vm_upto<kMaxInFlight>(p + 1 < nph ? per_phase : 0);
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      compute(p, p + 2 < nph ? p + 2 : -1);
+      compiler_fence();
+    }
+  } else if (wave >= NW) {
+    // copying waves: the phase's barrier once its copies have landed, then
+    // the copies of phase p + 2
+    issue(0);
+    if (nph > 1) issue(1);
+    for (int p = 0; p < nph; ++p) {
+      wait_vm_upto<kMaxInFlight>(p + 1 < nph ? per_phase : 0);
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      if (p + 2 < nph) issue(p + 2);
+    }
+  } else {
+    for (int p = 0; p < nph; ++p) {
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      compute(p, -1);
+      compiler_fence();
+    }
   }
 
   // Sum the eight waves' partial tiles (the ring is free once every wave has
   // passed this barrier).
   __syncthreads();
   float4_t* red = reinterpret_cast<float4_t*>(tsm);
+  if (wave < NW) {
 #pragma unroll
-  for (int i = 0; i < T; ++i)
+    for (int i = 0; i < T; ++i)
 #pragma unroll
-    for (int t = 0; t < AT; ++t) red[((i * AT + t) * NW + wave) * kWave + lane] = acc[i][t];
+      for (int t = 0; t < AT; ++t) red[((i * AT + t) * NW + wave) * kWave + lane] = acc[i][t];
+  }
   __syncthreads();
   const float* rf = reinterpret_cast<const float*>(tsm);
   const int O = T * 16 * m;
@@ -278,12 +306,12 @@ __global__ __launch_bounds__(NW * kWave, 1) void gemv_tile_kernel(
 
 constexpr int kTLdsMax = 160 * 1024;
 
-template <int T, int AT, int PB, int NW = (PB == 32 ? 16 : 8)>
+template <int T, int AT, int PB, int NW = 8, int NP = 4>
 hipError_t launch_tile_t(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
                          int64_t n, int64_t k, hipStream_t s) {
-  using G = TileGeo<T, AT, PB, NW>;
+  using G = TileGeo<T, AT, PB, NW, NP>;
   static_assert(G::lds <= kTLdsMax, "LDS budget");
-  const void* fn = reinterpret_cast<const void*>(&gemv_tile_kernel<T, AT, PB, NW>);
+  const void* fn = reinterpret_cast<const void*>(&gemv_tile_kernel<T, AT, PB, NW, NP>);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     const hipError_t e =
