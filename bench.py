@@ -284,7 +284,7 @@ def traffic_summary(fetch_csv, write_csv, out_path):
     def classify(name):
         if "neg_kernel" in name:
             return "calib_copy"
-        if "gemv_stream_kernel" in name or "gemv_rowwave_kernel" in name:
+        if "gemv_" in name and "_kernel" in name:
             return "gemv"
         if "quantize_kernel" in name:
             return "quantize_fp32_5120x5120"
@@ -331,6 +331,34 @@ def traffic_summary(fetch_csv, write_csv, out_path):
     return data
 
 
+def trace_summary(trace_csv, steps):
+    """Per batch size, the mean duration of the GEMV dispatches that bench_gemv
+    times, from a rocprofv3 kernel-trace CSV of a default run: the last
+    3 steps len(ms) GEMV dispatches are, per batch size in WORKLOADS[2].ms
+    order, `steps` eager launches (capture), `steps` in the warm replay and
+    `steps` in the timed replay."""
+    import csv
+    import synth
+    ms = list(synth.WORKLOADS[2].ms)
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+            if "gemv_" in name and "_kernel" in name:
+                start = int(r.get("Start_Timestamp") or r.get("Start-Timestamp"))
+                end = int(r.get("End_Timestamp") or r.get("End-Timestamp"))
+                rows.append((start, end - start, name))
+    rows.sort()
+    tail = rows[-3 * steps * len(ms):]
+    out = []
+    for i, m in enumerate(ms):
+        rep = tail[(3 * i + 2) * steps:(3 * i + 3) * steps]
+        names = sorted({r[2] for r in rep})
+        out.append({"m": m, "dispatches": len(rep), "mean_us": float(np.mean([r[1] for r in rep])) / 1e3,
+                    "kernels": names})
+    return out
+
+
 def cpu_baseline(w_host, n, k, ms, budget_s=12.0):
     """The oracle, untuned, on the decode step (all four batch sizes)."""
     import oracle
@@ -371,8 +399,14 @@ def main():
                     help="run the launches the FETCH_SIZE / WRITE_SIZE counter passes read")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from the two counter passes")
+    ap.add_argument("--trace-summary", metavar="TRACE_CSV",
+                    help="print per-batch-size GEMV durations from a kernel-trace CSV of a default run")
     args = ap.parse_args()
 
+    if args.trace_summary:
+        for r in trace_summary(args.trace_summary, args.steps):
+            print(json.dumps(r))
+        return
     if args.traffic_summary:
         d = traffic_summary(args.traffic_summary[0], args.traffic_summary[1],
                             ROOT / "profiles" / "traffic.json")
