@@ -155,7 +155,10 @@ struct WUnit {
 template <int BM, int BN, int WVM, int WVN, typename YT>
 __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, YT* __restrict__ y,
-    int64_t m, int64_t n, int64_t k) {
+    int64_t m, int64_t n, int64_t k, int64_t ldy, int kps, int64_t zstride) {
+  // k: full K (row strides).  Workgroups with blockIdx.z = z take the K steps
+  // z kps .. min((z + 1) kps, k / 64) - 1 and write y + z zstride (a split-K
+  // partial when gridDim.z > 1).
   constexpr int NTH = WVM * WVN * 64;       // threads
   constexpr int WM = BM / WVM, WN = BN / WVN;  // wave tile
   constexpr int TM = WM / 32, TN = WN / 32; // 32 x 32 products per wave
@@ -174,7 +177,12 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
   const int64_t rb = (k / kQK) * kBlockBytes;
-  const int nks = static_cast<int>(k / kBK);
+  const int ks0 = static_cast<int>(blockIdx.z) * kps;
+  const int nks_all = static_cast<int>(k / kBK);
+  const int nks = nks_all - ks0 < kps ? nks_all - ks0 : kps;
+  x += static_cast<int64_t>(ks0) * kBK;
+  W += static_cast<int64_t>(ks0) * 2 * kBlockBytes;
+  y += static_cast<int64_t>(blockIdx.z) * zstride;
 
   // Activation copies: copy i of this thread is LDS piece P = NTH i + tid
   // (row P / 8, swizzled column P % 8); the source column undoes the swizzle.
@@ -361,38 +369,114 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * WM + 32 * i + 8 * (r / 4) + 4 * kg + (r & 3);
         const int64_t col = n0 + wn * WN + 32 * j + (lane & 31);
-        if (row < m && col < n) y[row * n + col] = static_cast<YT>(acc[i][j][r]);
+        if (row < m && col < n) y[row * ldy + col] = static_cast<YT>(acc[i][j][r]);
       }
 }
 
+// Output columns c0 .. c0 + nc - 1 (weight rows c0 ..) into yc (their first
+// column, row stride ldy); with splits > 1, split z of K goes to yc + z zstride.
 template <int BM, int BN, int WVM, int WVN, typename YT>
-hipError_t launch_tiled(const half_t* x, const uint8_t* packed, YT* y, int64_t m, int64_t n,
-                        int64_t k, hipStream_t s) {
-  void* argv[] = {const_cast<const half_t**>(&x), const_cast<const uint8_t**>(&packed), &y, &m,
-                  &n, &k};
-  const dim3 grid(static_cast<unsigned>((n + BN - 1) / BN), static_cast<unsigned>((m + BM - 1) / BM));
+hipError_t launch_tiled(const half_t* x, const uint8_t* packed, int64_t c0, int64_t nc, YT* yc,
+                        int64_t m, int64_t k, int64_t ldy, int splits, int kps, int64_t zstride,
+                        hipStream_t s) {
+  const uint8_t* w = packed + c0 * ((k / kQK) * kBlockBytes);
+  void* argv[] = {const_cast<const half_t**>(&x), const_cast<const uint8_t**>(&w), &yc, &m,
+                  &nc, &k, &ldy, &kps, &zstride};
+  const dim3 grid(static_cast<unsigned>((nc + BN - 1) / BN), static_cast<unsigned>((m + BM - 1) / BM),
+                  static_cast<unsigned>(splits));
   return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, WVM, WVN, YT>),
                          grid, dim3(WVM * WVN * 64), argv, 0, s);
 }
 
+// y[r][c] = sum over z of part[z][r][c] (fixed order), 4 columns per thread.
+template <typename YT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, YT* __restrict__ y,
+                                                           int64_t m, int64_t nc, int64_t ldy, int splits) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // quad index
+  const int64_t quads = m * nc / 4;
+  if (q >= quads) return;
+  const int64_t e = 4 * q, r = e / nc, c = e - r * nc;
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < splits; ++z) acc += *reinterpret_cast<const float4_t*>(part + z * m * nc + e);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[r * ldy + c + i] = static_cast<YT>(acc[i]);
+}
+
+// Launch plan: main tiles (256 x 256 with 8 waves for m >= 1024, else
+// 128 x 128 with 4) over the leading n_main columns in whole rounds of one
+// tile per compute unit.  When a partial round would be left, the remaining
+// columns use the same tiles with K split `splits` ways so that the tail fills
+// the compute units; the fp32 partials go to the workspace and one reduction
+// sums them in split order.
+struct GemmPlan {
+  bool big = false;
+  int64_t n_main = 0;
+  int splits = 1, kps = 0;
+  size_t ws_bytes = 0;
+};
+
+GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
+  GemmPlan p;
+  p.big = m >= 1024;
+  const int bm = p.big ? 256 : 128, bn = p.big ? 256 : 128;
+  const int64_t cu = device_cu_count();
+  const int64_t tm = (m + bm - 1) / bm, tn = (n + bn - 1) / bn;
+  const int nks = static_cast<int>(k / kBK);
+  p.n_main = n;
+  p.kps = nks;
+  if (k % kBK != 0 || tm * tn <= cu || (tm * tn) % cu == 0 || (n % 4) != 0) return p;
+  const int64_t tn_main = (tm * tn / cu) * cu / tm;  // column tiles in whole rounds
+  if (tn_main < 1 || tn_main >= tn) return p;
+  const int64_t nt = n - tn_main * bn;
+  const int64_t tail_tiles = tm * ((nt + bn - 1) / bn);
+  int64_t splits = cu / tail_tiles;
+  if (splits > nks) splits = nks;
+  if (splits < 2) return p;
+  const int kps = static_cast<int>((nks + splits - 1) / splits);
+  p.n_main = tn_main * bn;
+  p.kps = kps;
+  p.splits = (nks + kps - 1) / kps;
+  p.ws_bytes = static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(nt) * 4;
+  return p;
+}
+
 template <typename YT>
 hipError_t dispatch_tiled(const half_t* x, const uint8_t* packed, YT* y, int64_t m, int64_t n,
-                          int64_t k, hipStream_t s) {
-  if (m >= 1024) return launch_tiled<256, 256, 2, 4, YT>(x, packed, y, m, n, k, s);
-  return launch_tiled<128, 128, 2, 2, YT>(x, packed, y, m, n, k, s);
+                          int64_t k, void* workspace, hipStream_t s) {
+  const GemmPlan p = gemm_plan(m, n, k);
+  const int nks = static_cast<int>(k / kBK);
+  hipError_t e = p.big ? launch_tiled<256, 256, 2, 4, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, s)
+                       : launch_tiled<128, 128, 2, 2, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, s);
+  if (e != hipSuccess || p.n_main == n) return e;
+  // Tail: split z of K writes part[z], m x nt with row stride nt.
+  const int64_t nt = n - p.n_main;
+  float* part = static_cast<float*>(workspace);
+  e = p.big ? launch_tiled<256, 256, 2, 4, float>(x, packed, p.n_main, nt, part, m, k, nt, p.splits,
+                                                  p.kps, m * nt, s)
+            : launch_tiled<128, 128, 2, 2, float>(x, packed, p.n_main, nt, part, m, k, nt, p.splits,
+                                                  p.kps, m * nt, s);
+  if (e != hipSuccess) return e;
+  const int64_t quads = m * nt / 4;
+  YT* yt = y + p.n_main;
+  int sp = p.splits;
+  int64_t ldy = n, mm = m, ntt = nt;
+  void* argv[] = {&part, &yt, &mm, &ntt, &ldy, &sp};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&splitk_reduce_kernel<YT>),
+                         dim3(static_cast<unsigned>((quads + 255) / 256)), dim3(256), argv, 0, s);
 }
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) { return gemm_plan(m, n, k).ws_bytes; }
 
 hipError_t launch_gemm(const void* x, DType, const uint8_t* packed, void* y,
-                       DType yt, int64_t m, int64_t n, int64_t k, void*,
+                       DType yt, int64_t m, int64_t n, int64_t k, void* workspace,
                        hipStream_t s) {
   const half_t* xp = static_cast<const half_t*>(x);
   if (k % kBK == 0) {
-    if (yt == DType::F16) return dispatch_tiled(xp, packed, static_cast<half_t*>(y), m, n, k, s);
-    return dispatch_tiled(xp, packed, static_cast<float*>(y), m, n, k, s);
+    if (yt == DType::F16)
+      return dispatch_tiled(xp, packed, static_cast<half_t*>(y), m, n, k, workspace, s);
+    return dispatch_tiled(xp, packed, static_cast<float*>(y), m, n, k, workspace, s);
   }
   const dim3 grid(static_cast<unsigned>((n + BN - 1) / BN),
                   static_cast<unsigned>((m + BM - 1) / BM));

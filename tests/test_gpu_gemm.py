@@ -149,3 +149,16 @@ def test_graph_replay_matches_eager(q4lib, gpu):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(to_host(y), eager), f"replay {rep}"
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 11000, 256), (1100, 14000, 128), (256, 17408, 512),
+                                   (2048, 17408, 64)])
+def test_main_and_tail_launches(q4lib, gpu, m, n, k):
+    """Shapes whose tile count leaves a partial round on 256 compute units: the
+    leading columns go to the main tiles in whole rounds and the rest to one
+    launch of smaller tiles (128x64 .. 32x32); every output is checked."""
+    w = synth.random_weights(3 * m + n + k, n, k, "student_t")
+    x = synth.random_activations(7 * m + k, m, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemm(q4lib, x, packed, n, k, "f16", gpu)
+    assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")
