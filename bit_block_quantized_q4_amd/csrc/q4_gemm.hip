@@ -146,10 +146,11 @@ constexpr int kRowBytes16 = 128;   // one tile row of 64 fp16 = 8 pieces of 16 b
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
 
-// One weight unit: 8 code bytes (half h of block b of a row) and the scale.
+// One weight unit: one block of a row (scale and 16 code bytes) as the
+// 20-byte aligned window w0..w4 that contains it.
 struct WUnit {
-  u32x3 w;     // 12-byte window that contains the 8 code bytes
-  uint32_t d;  // fp16 scale in the low half
+  u32x4 w;     // w0 .. w3
+  uint32_t w4;
 };
 
 template <int BM, int BN, int WVM, int WVN, typename YT>
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
   constexpr int B_STAGE = BN * kRowBytes16;
   constexpr int STAGE = A_STAGE + B_STAGE;
   constexpr int A_COPIES = BM * 8 / NTH;    // 16-byte copies per thread per step
-  constexpr int UNITS = BN * 4 / NTH;       // weight units per thread per step
+  constexpr int UNITS = BN * 2 / NTH;       // weight units (blocks) per thread per step
   static_assert(A_COPIES >= 1 && UNITS >= 1, "tile too small");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
@@ -202,37 +203,32 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
       dma16(asrc[i] + static_cast<int64_t>(ks) * kBK, dst + (NTH * i + 64 * wave) * 16);
   };
 
-  // Weight units: unit u of this thread is U = NTH u + tid: row U / 4,
-  // block (U / 2) % 2 of the step, half U % 2 (code bytes 8h .. 8h+7).
+  // Weight units: unit u of this thread is U = NTH u + tid: row U / 2, block
+  // U % 2 of the step.  A step is 36 bytes of the row starting 4-byte aligned
+  // (rows are 36-byte multiples here); block 0's window is its first 20
+  // bytes, block 1's the last 20, so both stay inside the step.  In the window
+  // the scale is at byte 2b and code byte c at 2 + 2b + c.
   const uint8_t* wsrc[UNITS];
-  const uint16_t* dsrc[UNITS];
-  uint32_t sel_even[UNITS], sel_odd[UNITS];
-  int wrow[UNITS], wpiece_lo[UNITS];
+  uint32_t sel_even[UNITS], sel_odd[UNITS], dshift[UNITS];
+  int wrow[UNITS], wblk[UNITS];
 #pragma unroll
   for (int u = 0; u < UNITS; ++u) {
     const int U = NTH * u + tid;
-    const int r = U >> 2;
-    const int b = (U >> 1) & 1;
-    const int h = U & 1;
+    const int r = U >> 1;
+    const int b = U & 1;
     const int64_t row = n0 + r < n ? n0 + r : n - 1;
-    const int64_t boff = row * rb + b * kBlockBytes;  // + 36 per step
-    const int64_t coff = boff + 2 + 8 * h;             // first code byte
-    // 12-byte aligned window holding the 8 code bytes at offset sh; it stays
-    // within the 36 bytes of the step (rows are 36-byte multiples here):
-    // aligned code bytes (coff % 4 == 0) take the window 4 bytes earlier.
-    const int sh = (coff & 3) ? 2 : 4;
-    wsrc[u] = W + (coff - sh);
-    dsrc[u] = reinterpret_cast<const uint16_t*>(W + boff);
-    // pair i' of the unit: window bytes sh + 2 i' and + 1, within dwords
-    // i'/2 .. i'/2 + 1; selectors for even / odd i' pick them as [c, 0, c', 0].
-    const uint32_t s0 = static_cast<uint32_t>(sh);
-    const uint32_t s1 = static_cast<uint32_t>(sh + 2);
+    wsrc[u] = W + row * rb + 16 * b;  // + 36 per step
+    // code pair i' (bytes 8h + 2i', +1) sits at byte 2 + 2b + 2 (i' & 1) of
+    // the dword pair {w[2h + i'/2 + 1] : w[2h + i'/2]}; selectors give [c, 0, c', 0]
+    const uint32_t s0 = static_cast<uint32_t>(2 + 2 * b);
+    const uint32_t s1 = s0 + 2;
     sel_even[u] = s0 | (0x0cu << 8) | ((s0 + 1) << 16) | (0x0cu << 24);
     sel_odd[u] = s1 | (0x0cu << 8) | ((s1 + 1) << 16) | (0x0cu << 24);
+    dshift[u] = 16u * b;
     wrow[u] = r;
-    wpiece_lo[u] = 4 * b + h;  // piece of the low nibbles; high nibbles: + 2
+    wblk[u] = b;
   }
-  // Untracked loads of the packed bytes of step ks (see load_dwordx3_untracked).
+  // Untracked loads of the packed bytes of step ks (see load_dwordx4_untracked).
   struct Units {
     WUnit v[UNITS];
   };
@@ -240,8 +236,9 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
     Units r;
 #pragma unroll
     for (int u = 0; u < UNITS; ++u) {
-      r.v[u].w = load_dwordx3_untracked(wsrc[u] + static_cast<int64_t>(ks) * 2 * kBlockBytes);
-      r.v[u].d = load_ushort_untracked(dsrc[u] + static_cast<int64_t>(ks) * kBlockBytes);
+      const uint8_t* src = wsrc[u] + static_cast<int64_t>(ks) * 2 * kBlockBytes;
+      r.v[u].w = load_dwordx4_untracked(src);
+      r.v[u].w4 = load_dword_untracked(src + 16);
     }
     return r;
   };
@@ -249,29 +246,33 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < UNITS; ++u) {
       tie_after(r.v[u].w);
-      tie_after(r.v[u].d);
+      tie_after(r.v[u].w4);
     }
   };
 
   const UnpackConsts kc = make_unpack_consts();
-  // Dequantise unit u (16 weights) and store its two pieces into `stage`.
-  auto dequant_store = [&](const WUnit& un, int u, int stage) {
-    const half2_t d2 = __builtin_bit_cast(half2_t, (un.d & 0xFFFFu) | (un.d << 16));
+  // Dequantise half h of unit u (16 weights) and store its two pieces into
+  // `stage`: codes 8h .. 8h+7 give k 8h .. 8h+7 (low nibbles, piece 4b + h)
+  // and k 16 + 8h .. (high nibbles, piece 4b + h + 2).
+  auto dequant_half = [&](const WUnit& un, int u, int h, int stage) {
+    const uint32_t w[5] = {un.w[0], un.w[1], un.w[2], un.w[3], un.w4};
+    const uint32_t dbits = (w[0] >> dshift[u]) & 0xFFFFu;
+    const half2_t d2 = __builtin_bit_cast(half2_t, dbits | (dbits << 16));
     const half2_t klo = {static_cast<half_t>(-1032.0f), static_cast<half_t>(-1032.0f)};
     const half2_t khi = {static_cast<half_t>(-72.0f), static_cast<half_t>(-72.0f)};
+    uint8_t* bs = smem + stage * STAGE + A_STAGE;
     u32x4 lo, hi;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t t = __builtin_amdgcn_perm(un.w[i / 2 + 1], un.w[i / 2],
+      const uint32_t t = __builtin_amdgcn_perm(w[2 * h + i / 2 + 1], w[2 * h + i / 2],
                                                (i & 1) ? sel_odd[u] : sel_even[u]);
       const half2_t ql = __builtin_bit_cast(half2_t, (t & kc.mask_lo) | kc.exp_lo) + klo;
       const half2_t qh = __builtin_bit_cast(half2_t, (t & kc.mask_hi) | kc.exp_hi) + khi;
       lo[i] = __builtin_bit_cast(uint32_t, ql * d2);
       hi[i] = __builtin_bit_cast(uint32_t, qh * d2);
     }
-    uint8_t* bs = smem + stage * STAGE + A_STAGE;
-    *reinterpret_cast<u32x4*>(bs + swz(wrow[u], wpiece_lo[u]) * 16) = lo;
-    *reinterpret_cast<u32x4*>(bs + swz(wrow[u], wpiece_lo[u] + 2) * 16) = hi;
+    *reinterpret_cast<u32x4*>(bs + swz(wrow[u], 4 * wblk[u] + h) * 16) = lo;
+    *reinterpret_cast<u32x4*>(bs + swz(wrow[u], 4 * wblk[u] + h + 2) * 16) = hi;
   };
 
   float16_t acc[TM][TN];
@@ -291,7 +292,10 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
     wait_vm<0>();
     tie_units(u0);
 #pragma unroll
-    for (int u = 0; u < UNITS; ++u) dequant_store(u0.v[u], u, 0);
+    for (int u = 0; u < UNITS; ++u) {
+      dequant_half(u0.v[u], u, 0, 0);
+      dequant_half(u0.v[u], u, 1, 0);
+    }
   }
   Units nxt = load_units(nks > 1 ? 1 : 0);
   wait_vm<0>();
@@ -325,38 +329,83 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
     }
   };
 
-  half8_t af[2][TM], bf[2][TN];
-  read_frags(smem, 0, af[0], bf[0]);
-  for (int ks = 0; ks < nks; ++ks) {
-    const int st = ks & 1;
-    // Activations of step ks + 1 into the other stage (the last step copies
-    // its own again: that stage is no longer read).
-    issue_a(ks + 1 < nks ? ks + 1 : ks, st ^ 1);
-    const Units cur = nxt;
-    nxt = load_units(ks + 2 < nks ? ks + 2 : nks - 1);
-    const uint8_t* as = smem + st * STAGE;
+  if constexpr (TM * TN <= 4) {
+    // Small wave tiles (one wave per SIMD): few products per k16 sub-step
+    // cannot cover an LDS read, so all four sub-steps' fragments of a stage
+    // are read right after its barrier and the products then run back to
+    // back, with the dequantisation interleaved.
+    half8_t fa[4][TM], fb[4][TN];
+    auto read_all = [&](const uint8_t* as) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {  // 16-wide k sub-steps
-      const int c = kk & 1;
-      if (kk < 3) read_frags(as, kk + 1, af[c ^ 1], bf[c ^ 1]);
+      for (int kk = 0; kk < 4; ++kk) read_frags(as, kk, fa[kk], fb[kk]);
+    };
+    auto interleave_valu = []() {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM * TN; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      }
+    };
+    read_all(smem);
+    for (int ks = 0; ks < nks; ++ks) {
+      const int st = ks & 1;
+      issue_a(ks + 1 < nks ? ks + 1 : ks, st ^ 1);
+      const Units cur = nxt;
+      nxt = load_units(ks + 2 < nks ? ks + 2 : nks - 1);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
-      // The next step's weights (on the last step: a harmless rewrite of the
-      // stage no longer read).
+      for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int u = 0; u < UNITS; ++u)
-        if (u % 4 == kk) dequant_store(cur.v[u], u, st ^ 1);
-      if (kk < 3) interleave(IC<true>{});
-      else interleave(IC<false>{});
-      __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u)
+          for (int h = 0; h < 2; ++h)
+            if ((2 * u + h) % 4 == kk) dequant_half(cur.v[u], u, h, st ^ 1);
+        interleave_valu();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_vm<0>();
+      tie_units(nxt);
+      __syncthreads();
+      read_all(smem + (st ^ 1) * STAGE);
     }
-    wait_vm<0>();
-    tie_units(nxt);
-    __syncthreads();
-    read_frags(smem + (st ^ 1) * STAGE, 0, af[0], bf[0]);
+  } else {
+    half8_t af[2][TM], bf[2][TN];
+    read_frags(smem, 0, af[0], bf[0]);
+    for (int ks = 0; ks < nks; ++ks) {
+      const int st = ks & 1;
+      // Activations of step ks + 1 into the other stage (the last step copies
+      // its own again: that stage is no longer read).
+      issue_a(ks + 1 < nks ? ks + 1 : ks, st ^ 1);
+      const Units cur = nxt;
+      nxt = load_units(ks + 2 < nks ? ks + 2 : nks - 1);
+      const uint8_t* as = smem + st * STAGE;
+  #pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {  // 16-wide k sub-steps
+        const int c = kk & 1;
+        if (kk < 3) read_frags(as, kk + 1, af[c ^ 1], bf[c ^ 1]);
+  #pragma unroll
+        for (int i = 0; i < TM; ++i)
+  #pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
+        // The next step's weights (on the last step: a harmless rewrite of the
+        // stage no longer read).
+  #pragma unroll
+        for (int u = 0; u < UNITS; ++u)
+          for (int h = 0; h < 2; ++h)
+            if ((2 * u + h) % 4 == kk) dequant_half(cur.v[u], u, h, st ^ 1);
+        if (kk < 3) interleave(IC<true>{});
+        else interleave(IC<false>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_vm<0>();
+      tie_units(nxt);
+      __syncthreads();
+      read_frags(smem + (st ^ 1) * STAGE, 0, af[0], bf[0]);
+    }
   }
 
   // 32x32 accumulator layout: lane l holds column l % 32; register r holds
