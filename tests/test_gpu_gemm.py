@@ -155,8 +155,9 @@ def test_graph_replay_matches_eager(q4lib, gpu):
                                    (2048, 17408, 64)])
 def test_main_and_tail_launches(q4lib, gpu, m, n, k):
     """Shapes whose tile count leaves a partial round on 256 compute units: the
-    leading columns go to the main tiles in whole rounds and the rest to one
-    launch of smaller tiles (128x64 .. 32x32); every output is checked."""
+    leading columns go to the main tiles in whole rounds, the rest to the same
+    tiles with K split across workgroups (fp32 partials in the workspace, then
+    a fixed-order reduction); every output is checked."""
     w = synth.random_weights(3 * m + n + k, n, k, "student_t")
     x = synth.random_activations(7 * m + k, m, k, "f16")
     packed = oracle.quantize(w)
