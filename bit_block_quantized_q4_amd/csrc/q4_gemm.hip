@@ -2,28 +2,34 @@
 //
 // The GPU path from Q4_0 weights onto matrix cores of the vertical-disaggregation page
 // (section "Every cycle counts: custom kernels"): long prompts are dense
-// computation, so weight tiles are dequantised once per workgroup into LDS as
-// fp16 w = (q - 8) * d (one rounding) and contracted with the fp16 activations
-// on v_mfma_f32_32x32x16_f16 with fp32 accumulation.  Each output element is
-// owned by exactly one lane and accumulated in a fixed k order, so results are
-// bit-reproducible.
+// computation, so weights are dequantised once per workgroup to fp16
+// w = (q - 8) * d (one rounding) and contracted with the fp16 activations on
+// v_mfma_f32_32x32x16_f16 with fp32 accumulation.  Every output is summed in a
+// fixed order (k order within one lane; for slice-K tiles the four slice
+// partials then in wave order; for split-K tails the splits in split order),
+// so results are bit-reproducible.
 //
-// Tiled kernel (k % 64 == 0)
-// --------------------------
-// A BM x BN output tile per workgroup of four wavefronts (2 x 2, each
-// BM/2 x BN/2), k steps of 64 (two Q4_0 blocks), two LDS stages:
-//   - activations: direct global->LDS copies (global_load_lds_dwordx4) of the
-//     BM x 64 fp16 tile, 16-byte pieces placed with an XOR swizzle
-//     (piece c of row r at r*8 + (c ^ (r & 7))) so that matrix-core operand
-//     reads hit distinct banks;
-//   - weights: each thread owns "units" of 8 code bytes of one row and one
-//     block (16 weights); the packed bytes of step s+1 are loaded into
-//     registers during step s-1..s, dequantised with byte permutes, the
-//     1024+q / 64+q exponent trick, an exact packed subtraction and one packed
-//     multiply by d, and written to the other stage in the same swizzle;
-//   - one barrier per k step; the step's matrix products interleave with the
-//     next step's dequantisation.
-// The generic kernel below handles k % 64 != 0.
+// Kernels
+// -------
+//   - gemm_mfma_kernel (k % 64 == 0): a BM x BN output tile per workgroup
+//     (256 x 256 with 8 waves, each 128 x 64, for m >= 1024; else 128 x 128
+//     with 4 waves of 64 x 64), k steps of 64 (two Q4_0 blocks), two LDS
+//     stages.  Activations arrive by direct global->LDS copies
+//     (global_load_lds_dwordx4) into an XOR swizzle (piece c of row r at
+//     r*8 + (c ^ (r & 7))) so that operand reads hit distinct banks.  Each
+//     thread owns weight units (one whole block of one row), loads them two
+//     steps ahead, dequantises them with byte permutes, the 1024+q / 64+q
+//     exponent trick, an exact packed subtraction and one packed multiply by
+//     d, and writes them into the other stage in the same swizzle, interleaved
+//     with the step's matrix products.  One barrier per step.
+//   - gemm_slicek_kernel (m < 1024, k % 256 == 0, k >= 1024): 128 x 128 tiles
+//     whose four waves each own the whole tile for one k16 slice of every
+//     step, with packed weights copied into LDS and dequantised in registers
+//     by the one wave that uses them; see its own comment.
+//   - gemm_tile_kernel: the generic LDS-tiled kernel for k % 64 != 0.
+// Launches run whole rounds of tiles on the compute units; a partial round's
+// columns run the same tiles with K split across workgroups (fp32 partials,
+// then splitk_reduce_kernel in split order).
 #include "q4_device.hpp"
 
 namespace q4 {
@@ -422,6 +428,274 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
       }
 }
 
+// ------------------------------------------------------------------ slice-K
+//
+// 128 x 128 output tile, four waves, k % 256 == 0.  Wave w owns the whole
+// tile for the k16 slice w of every 64-wide k step: k 16w .. 16w+15, which is
+// one nibble half (w & 1) of block w >> 1 of the step.  Every activation and
+// weight element is therefore read from LDS by one wave only and dequantised
+// once, and a wave's operand fragments per step are four of each (against
+// eight for a 2 x 2 split of the tile).  The four partial tiles are summed in
+// wave order at the end.
+//
+// Copies (global -> LDS, 16-byte pieces, issued by all waves):
+//   - activations: a ring of four 64-wide k stages, stage s of step ks = ks % 4,
+//     refilled four steps ahead;
+//   - packed weights: the 144 bytes of each row that cover four steps (256 k,
+//     16-byte aligned because k % 256 == 0), a ring of two.
+// Per step: issue copies, read the next step's activation fragments and the
+// raw weights of the step after, run this step's 16 matrix products
+// interleaved with those reads and with the dequantisation of the next
+// step's weights (read one step earlier, so no arithmetic waits on a fresh
+// LDS read), then one barrier once the copies the next step reads have
+// landed.
+constexpr int kSkAStage = 128 * kRowBytes16;        // 16 KB
+constexpr int kSkSeg = 4 * 2 * kBlockBytes;         // 144 packed bytes per row and 4 steps
+constexpr int kSkWStage = 128 * kSkSeg;             // 18 KB
+constexpr int kSkWOff = 4 * kSkAStage;              // weight ring after the activation ring
+constexpr int kSkLds = kSkWOff + 2 * kSkWStage;     // 100 KB
+constexpr int kSkRedCol = 36;                       // floats per column of a partial (32 rows + pad)
+static_assert(4 * 128 * kSkRedCol * 4 <= kSkLds, "reduction buffer");
+
+template <typename YT>
+__global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
+    const half_t* __restrict__ x, const uint8_t* __restrict__ W, YT* __restrict__ y,
+    int64_t m, int64_t n, int64_t k, int64_t ldy, int kps, int64_t zstride) {
+  // k: full K (row strides).  Workgroups with blockIdx.z = z take the k steps
+  // z kps .. min((z + 1) kps, k / 64) - 1 (kps % 4 == 0) and write y + z zstride.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSkLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = lane >> 5, lc = lane & 31;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 128;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 128;
+  const int64_t rb = (k / kQK) * kBlockBytes;
+  const int ks0 = static_cast<int>(blockIdx.z) * kps;
+  const int nks_all = static_cast<int>(k / kBK);
+  const int nks = nks_all - ks0 < kps ? nks_all - ks0 : kps;  // a multiple of 4
+  const int nss = nks >> 2;
+  x += static_cast<int64_t>(ks0) * kBK;
+  W += static_cast<int64_t>(ks0) * 2 * kBlockBytes;
+  y += static_cast<int64_t>(blockIdx.z) * zstride;
+
+  // Activation copy i of this thread: LDS piece P = 256 i + tid of a stage
+  // (row P / 8, swizzled column P % 8).
+  const half_t* asrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int P = 256 * i + tid;
+    const int r = P >> 3;
+    const int c = (P & 7) ^ (r & 7);
+    const int64_t row = m0 + r < m ? m0 + r : m - 1;
+    asrc[i] = x + row * k + 8 * c;
+  }
+  auto issue_a = [&](int ks, int stage) {
+    uint8_t* dst = smem + stage * kSkAStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dma16(asrc[i] + static_cast<int64_t>(ks) * kBK, dst + (256 * i + 64 * wave) * 16);
+  };
+  // Weight copy i of this thread: piece p of a weight stage (row p / 9, piece
+  // p % 9 of its 144 bytes); 1152 pieces = four full rounds of 256 plus a
+  // fifth in which each wave copies 32.
+  const uint8_t* wsrc[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int p = i < 4 ? 256 * i + tid : 1024 + 32 * wave + lc;
+    const int r = p / 9;
+    const int c = p - 9 * r;
+    const int64_t row = n0 + r < n ? n0 + r : n - 1;
+    wsrc[i] = W + row * rb + 16 * c;
+  }
+  auto issue_w = [&](int ss, int buf) {
+    uint8_t* dst = smem + kSkWOff + buf * kSkWStage;
+    const int64_t off = static_cast<int64_t>(ss) * kSkSeg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + off, dst + (256 * i + 64 * wave) * 16);
+    if (lane < 32) dma16(wsrc[4] + off, dst + (1024 + 32 * wave) * 16);
+  };
+
+  // This wave's share of a step: block b = w >> 1 of the step and its code
+  // bytes 8h .. 8h + 7 (h = w & 1), both nibbles.  The k order inside a
+  // matrix product is free as long as both operands follow it: lane (lc, kg)
+  // takes the low nibbles (kg = 0, block elements 8h .. 8h + 7) or the high
+  // nibbles (kg = 1, elements 16 + 8h ..) of those bytes, and its activation
+  // fragment is the matching 8 halves, piece 4b + 2kg + h of the step.  Both
+  // halves of the wave read the same weight bytes (one LDS broadcast): the
+  // aligned 12-byte window at step byte 16b + 8h (code byte 8h + e at window
+  // byte O + e, O = 2 + 2b) and the scale as the dword at 16b (its low half
+  // for b = 0, high half for b = 1).
+  const int b = wave >> 1, h = wave & 1;
+  const uint32_t O = 2u + 2u * static_cast<uint32_t>(b);
+  const uint32_t sel_a = O | (0x0cu << 8) | ((O + 1) << 16) | (0x0cu << 24);
+  const uint32_t sel_b = (O + 2) | (0x0cu << 8) | ((O + 3) << 16) | (0x0cu << 24);
+  const uint32_t nib_mask = kg ? 0x00F000F0u : 0x000F000Fu;
+  const uint32_t nib_exp = kg ? 0x54005400u : 0x64006400u;  // fp16 64 + q / 1024 + q
+  const half_t sub1 = static_cast<half_t>(kg ? -72.0f : -1032.0f);
+  const half2_t nib_sub = {sub1, sub1};
+  const uint32_t dshift = 16u * static_cast<uint32_t>(b);
+  const int apiece = 4 * b + 2 * kg + h;
+
+  struct Raw {
+    uint32_t w[4][3];
+    uint32_t d[4];
+  };
+  // Reads past the last step are of valid LDS addresses and unused.
+  auto read_a = [&](int ks, half8_t (&fa)[4]) {
+    const uint8_t* as = smem + (ks & 3) * kSkAStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fa[i] = *reinterpret_cast<const half8_t*>(as + swz(32 * i + lc, apiece) * 16);
+  };
+  auto read_w = [&](int ks, Raw& raw) {
+    const uint8_t* ws = smem + kSkWOff + ((ks >> 2) & 1) * kSkWStage + 36 * (ks & 3) + 16 * b;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint8_t* rp = ws + (32 * jj + lc) * kSkSeg;
+      const uint32_t* win = reinterpret_cast<const uint32_t*>(rp + 8 * h);
+      raw.w[jj][0] = win[0];
+      raw.w[jj][1] = win[1];
+      raw.w[jj][2] = win[2];
+      raw.d[jj] = *reinterpret_cast<const uint32_t*>(rp);
+    }
+  };
+  auto dequant = [&](const Raw& raw, half8_t (&fb)[4]) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t db = (raw.d[jj] >> dshift) & 0xFFFFu;
+      const half2_t d2 = __builtin_bit_cast(half2_t, db | (db << 16));
+      const uint32_t w0 = raw.w[jj][0], w1 = raw.w[jj][1], w2 = raw.w[jj][2];
+      const uint32_t t[4] = {__builtin_amdgcn_perm(w1, w0, sel_a), __builtin_amdgcn_perm(w1, w0, sel_b),
+                             __builtin_amdgcn_perm(w2, w1, sel_a), __builtin_amdgcn_perm(w2, w1, sel_b)};
+      u32x4 r;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const half2_t v = __builtin_bit_cast(half2_t, (t[q] & nib_mask) | nib_exp) + nib_sub;
+        r[q] = __builtin_bit_cast(uint32_t, v * d2);
+      }
+      fb[jj] = __builtin_bit_cast(half8_t, r);
+    }
+  };
+
+  float16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Prologue: copies in the order the loop's waits assume (A0 W0 A1 A2 W1
+  // A3); once A0, W0 and A1 have landed: step 0's operands, step 1's raw
+  // weights, then a barrier before step 0 refills stage 0.
+  const int last = nks - 1;
+  issue_a(0, 0);
+  issue_w(0, 0);
+  issue_a(1 < last ? 1 : last, 1);
+  issue_a(2 < last ? 2 : last, 2);
+  issue_w(1 < nss - 1 ? 1 : nss - 1, 1);
+  issue_a(3 < last ? 3 : last, 3);
+  wait_vm_lgkm0<13>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  half8_t fa[4], fb[4];
+  Raw rc;  // raw weights of step ks + 1
+  {
+    Raw r0;
+    read_a(0, fa);
+    read_w(0, r0);
+    read_w(1, rc);
+    dequant(r0, fb);
+  }
+  wait_vm_lgkm0<13>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+
+  // Step ks = 4 ss + j works on operands in registers and, for the steps
+  // ahead, reads step ks + 1's activation fragments and step ks + 2's raw
+  // weights and dequantises step ks + 1's.  Copies: A(ks + 4) into stage j
+  // (read last during step ks - 1), and at j = 2 weight stage ss + 2 into
+  // buffer ss & 1 (read last during step ks - 1).  The wait before the
+  // barrier leaves in flight only copies issued after those the next step
+  // reads: A(ks + 2), and at j = 1 also W(ss + 1).
+  for (int ss = 0; ss < nss; ++ss) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ks = 4 * ss + j;
+      issue_a(ks + 4 < last ? ks + 4 : last, j);
+      if (j == 2) issue_w(ss + 2 < nss - 1 ? ss + 2 : nss - 1, ss & 1);
+      half8_t na[4], nb[4];
+      Raw rn;
+      read_a(ks + 1, na);
+      read_w(ks + 2, rn);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
+      dequant(rc, nb);
+      // each product followed by one fragment read and a share of the
+      // dequantisation
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tie_after(nb[i]);  // dequantised within this step, not sunk into the next
+        fa[i] = na[i];
+        fb[i] = nb[i];
+      }
+      rc = rn;
+      __builtin_amdgcn_sched_barrier(0);
+      if (j == 1) wait_vm_lgkm0<8>();
+      else wait_vm_lgkm0<13>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      compiler_fence();
+    }
+  }
+  wait_vm_lgkm0<0>();
+  __syncthreads();
+
+  // Sum the four partial tiles, one 32-row fragment row at a time: each wave
+  // writes its partial column-major (column stride kSkRedCol floats), then
+  // thread t sums column t % 128, rows 16 (t / 128) .. + 15 in wave order.
+  float* red = reinterpret_cast<float*>(smem);
+  const int scol = tid & 127, srow = 16 * (tid >> 7);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4_t v = {acc[i][jj][4 * q], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2], acc[i][jj][4 * q + 3]};
+        *reinterpret_cast<float4_t*>(red + (wave * 128 + 32 * jj + lc) * kSkRedCol + 8 * q + 4 * kg) = v;
+      }
+    __syncthreads();
+    float4_t s4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s4[q] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        s4[q] += *reinterpret_cast<const float4_t*>(red + (w * 128 + scol) * kSkRedCol + srow + 4 * q);
+    const int64_t col = n0 + scol;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + 32 * i + srow + 4 * q + e;
+        if (row < m && col < n) y[row * ldy + col] = static_cast<YT>(s4[q][e]);
+      }
+    __syncthreads();
+  }
+}
+
 // Output columns c0 .. c0 + nc - 1 (weight rows c0 ..) into yc (their first
 // column, row stride ldy); with splits > 1, split z of K goes to yc + z zstride.
 template <int BM, int BN, int WVM, int WVN, typename YT>
@@ -435,6 +709,19 @@ hipError_t launch_tiled(const half_t* x, const uint8_t* packed, int64_t c0, int6
                   static_cast<unsigned>(splits));
   return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, WVM, WVN, YT>),
                          grid, dim3(WVM * WVN * 64), argv, 0, s);
+}
+
+template <typename YT>
+hipError_t launch_slicek(const half_t* x, const uint8_t* packed, int64_t c0, int64_t nc, YT* yc,
+                         int64_t m, int64_t k, int64_t ldy, int splits, int kps, int64_t zstride,
+                         hipStream_t s) {
+  const uint8_t* w = packed + c0 * ((k / kQK) * kBlockBytes);
+  void* argv[] = {const_cast<const half_t**>(&x), const_cast<const uint8_t**>(&w), &yc, &m,
+                  &nc, &k, &ldy, &kps, &zstride};
+  const dim3 grid(static_cast<unsigned>((nc + 127) / 128), static_cast<unsigned>((m + 127) / 128),
+                  static_cast<unsigned>(splits));
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_slicek_kernel<YT>), grid, dim3(256),
+                         argv, 0, s);
 }
 
 // y[r][c] = sum over z of part[z][r][c] (fixed order), 4 columns per thread.
@@ -452,13 +739,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 // Launch plan: main tiles (256 x 256 with 8 waves for m >= 1024, else
-// 128 x 128 with 4) over the leading n_main columns in whole rounds of one
-// tile per compute unit.  When a partial round would be left, the remaining
+// 128 x 128 with 4: slice-K when k % 256 == 0 and k >= 1024) over the
+// leading n_main columns in whole rounds of one tile per compute unit.  When a partial round would be left, the remaining
 // columns use the same tiles with K split `splits` ways so that the tail fills
 // the compute units; the fp32 partials go to the workspace and one reduction
 // sums them in split order.
 struct GemmPlan {
   bool big = false;
+  bool slicek = false;  // 128 x 128 slice-K tiles (k % 256 == 0)
   int64_t n_main = 0;
   int splits = 1, kps = 0;
   size_t ws_bytes = 0;
@@ -467,6 +755,7 @@ struct GemmPlan {
 GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
   GemmPlan p;
   p.big = m >= 1024;
+  p.slicek = !p.big && k % 256 == 0 && k >= 1024;  // short k: prologue and reduction dominate
   const int bm = p.big ? 256 : 128, bn = p.big ? 256 : 128;
   const int64_t cu = device_cu_count();
   const int64_t tm = (m + bm - 1) / bm, tn = (n + bn - 1) / bn;
@@ -481,7 +770,8 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
   int64_t splits = cu / tail_tiles;
   if (splits > nks) splits = nks;
   if (splits < 2) return p;
-  const int kps = static_cast<int>((nks + splits - 1) / splits);
+  int kps = static_cast<int>((nks + splits - 1) / splits);
+  if (p.slicek) kps = (kps + 3) / 4 * 4;  // whole 4-step weight segments
   p.n_main = tn_main * bn;
   p.kps = kps;
   p.splits = (nks + kps - 1) / kps;
@@ -494,16 +784,19 @@ hipError_t dispatch_tiled(const half_t* x, const uint8_t* packed, YT* y, int64_t
                           int64_t k, void* workspace, hipStream_t s) {
   const GemmPlan p = gemm_plan(m, n, k);
   const int nks = static_cast<int>(k / kBK);
-  hipError_t e = p.big ? launch_tiled<256, 256, 2, 4, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, s)
-                       : launch_tiled<128, 128, 2, 2, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, s);
+  hipError_t e = p.big      ? launch_tiled<256, 256, 2, 4, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, s)
+                 : p.slicek ? launch_slicek<YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, s)
+                            : launch_tiled<128, 128, 2, 2, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, s);
   if (e != hipSuccess || p.n_main == n) return e;
   // Tail: split z of K writes part[z], m x nt with row stride nt.
   const int64_t nt = n - p.n_main;
   float* part = static_cast<float*>(workspace);
-  e = p.big ? launch_tiled<256, 256, 2, 4, float>(x, packed, p.n_main, nt, part, m, k, nt, p.splits,
-                                                  p.kps, m * nt, s)
-            : launch_tiled<128, 128, 2, 2, float>(x, packed, p.n_main, nt, part, m, k, nt, p.splits,
-                                                  p.kps, m * nt, s);
+  e = p.big      ? launch_tiled<256, 256, 2, 4, float>(x, packed, p.n_main, nt, part, m, k, nt,
+                                                      p.splits, p.kps, m * nt, s)
+      : p.slicek ? launch_slicek<float>(x, packed, p.n_main, nt, part, m, k, nt, p.splits, p.kps,
+                                        m * nt, s)
+                 : launch_tiled<128, 128, 2, 2, float>(x, packed, p.n_main, nt, part, m, k, nt,
+                                                      p.splits, p.kps, m * nt, s);
   if (e != hipSuccess) return e;
   const int64_t quads = m * nt / 4;
   YT* yt = y + p.n_main;

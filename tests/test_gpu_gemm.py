@@ -163,3 +163,17 @@ def test_main_and_tail_launches(q4lib, gpu, m, n, k):
     packed = oracle.quantize(w)
     g = run_gemm(q4lib, x, packed, n, k, "f16", gpu)
     assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 100, 1024), (33, 4097, 1280), (129, 300, 2048), (255, 1000, 1536),
+                                   (300, 11000, 1024), (700, 9000, 3072)])
+def test_slice_k_tiles(q4lib, gpu, m, n, k):
+    """m < 1024, k % 256 == 0, k >= 1024: 128 x 128 tiles whose four waves each
+    take one k16 slice of every step; ragged rows and columns, an odd number of
+    256-wide weight segments (k = 1280), a split-K tail whose splits hold one
+    segment each (300 x 11000 x 1024) and a launch with no tail (700 x 9000)."""
+    w = synth.random_weights(5 * m + n + k, n, k, "student_t")
+    x = synth.random_activations(11 * m + k, m, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemm(q4lib, x, packed, n, k, "f32", gpu)
+    assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")
