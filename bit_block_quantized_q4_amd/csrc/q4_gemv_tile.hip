@@ -2,13 +2,16 @@
 // for a batch of up to 32 activation rows (llama.cpp's Q4_0 block page, block
 // layout; the serving page's batched decode step).
 //
-// One workgroup owns 16 T consecutive weight rows over the whole of K, so no
-// partial sums leave the workgroup.  K is walked in phases of PB blocks
-// (32 PB weights).  For every phase the eight waves copy, global -> LDS, the
-// phase's weight bytes of the 16 T rows and the phase's activation columns
-// (16-byte copies); three phases are resident in a ring, so the
-// copies of phase p + 2 are in flight while phase p is computed.  Within a
-// phase wave w owns blocks w PB / 8 .. (w + 1) PB / 8 - 1 for all 16 T rows;
+// One workgroup owns R <= 16 T consecutive weight rows over the whole of K,
+// so no partial sums leave the workgroup.  When R is not a multiple of 16
+// (rows spread over every compute unit) the last row tile is partial: its
+// unfilled rows hold stale bytes, feed only their own outputs and are never
+// stored.  K is walked in phases of PB blocks (32 PB weights).  For every
+// phase four copying waves copy, global -> LDS, the phase's weight bytes of
+// the R rows and the phase's activation columns (16-byte copies); three
+// phases are resident in a ring, so the copies of phases p + 1 and p + 2 are
+// in flight while eight computing waves work on phase p.  Within a phase
+// wave w owns blocks w PB / 8 .. (w + 1) PB / 8 - 1 for all 16 T rows;
 // each (row tile, block) pair is one v_mfma_f32_16x16x32_f16 with 16
 // activation rows on the A side and 16 weight rows on the B side.  The block's
 // 32 codes enter as fp16 subnormals q 2^-24 (the nibble is the whole
@@ -29,7 +32,12 @@
 namespace q4 {
 namespace {
 
-constexpr int kTSlots = 3;   // phases resident in LDS
+constexpr int kTLdsMax = 160 * 1024;
+// Phases resident in LDS.  (Deeper rings of smaller phases, 16 blocks in up
+// to seven slots, measured slower than three slots of 32 blocks at
+// 5120 x 5120: the per-phase barrier and fixed costs outweigh the extra
+// copies in flight.)
+constexpr int kTSlots = 3;
 
 template <int V>
 struct TC {
@@ -76,10 +84,13 @@ struct TileGeo {
   static_assert(xp >= 16, "swizzle needs 16 pieces per row");
 };
 
-template <int T, int AT, int PB, int NW, int NP>
+// FULL: every workgroup owns 16 T rows (the last one's rows past n copy row
+// n - 1 and are not stored); otherwise R = rows < 16 T rows and only those
+// are copied (a run-time bound on the copies).
+template <int T, int AT, int PB, bool FULL, int NW, int NP>
 __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, void* __restrict__ y, int m,
-    int64_t n, int64_t k, int y_f16) {
+    int64_t n, int64_t k, int y_f16, int rows) {
   using G = TileGeo<T, AT, PB, NW, NP>;
   constexpr int CW = G::cwaves;
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
@@ -87,21 +98,24 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   // copying-wave index (waves NW .. NW + NP - 1 copy when NP > 0)
   const int cwave = NP > 0 ? (wave >= NW ? wave - NW : 0) : wave;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * (16 * T);
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows;
+  const int rv = static_cast<int>(n - row0 < rows ? n - row0 : rows);  // rows stored
   const int64_t rb = (k / kQK) * kBlockBytes;  // bytes per weight row
   const int nph = static_cast<int>(k / G::phase_k);
   const uint32_t smem = lds_addr(tsm);
 
   // Weight copies.  Slot piece i = (q CW + cwave) 64 + lane holds piece
   // i % wstride_pc of the phase's segment of row i / wstride_pc (the padding
-  // piece repeats the last one; rows past n read row n - 1, computed and
-  // never stored).  Lanes past the slot's pieces copy nothing; a wave issues
-  // the rounds q in which any of its lanes copies (cw of them).
+  // piece repeats the last one).  FULL: all 16 T rows are copied (rows past
+  // n read row n - 1); otherwise only the rv rows of the workgroup.  Lanes
+  // past the copied pieces copy nothing, and a wave issues the rounds q in
+  // which any of its lanes copies (cw of them).
+  const int wpos = FULL ? G::wpos : rv * G::wstride_pc;
   uint32_t wsrc[G::niw];
 #pragma unroll
   for (int q = 0; q < G::niw; ++q) {
     int i = (q * CW + cwave) * kWave + lane;
-    if (i > G::wpos - 1) i = G::wpos - 1;
+    if (i > wpos - 1) i = wpos - 1;
     const int r = i / G::wstride_pc;
     int c = i - r * G::wstride_pc;
     if (c > G::row_pc - 1) c = G::row_pc - 1;
@@ -111,7 +125,7 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
   }
   int cw = 0;
 #pragma unroll
-  for (int q = 0; q < G::niw; ++q) cw += ((q * CW + cwave) * kWave < G::wpos) ? 1 : 0;
+  for (int q = 0; q < G::niw; ++q) cw += ((q * CW + cwave) * kWave < wpos) ? 1 : 0;
   // Activation copies: piece position i of the slot's activation area holds
   // piece (i % xp) ^ (row & 15) of row i / xp of the phase's columns; only
   // the m real rows are copied (a wave issues the cx rounds in which any of
@@ -140,7 +154,7 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
     if constexpr (c < G::niw) {
       const int i0 = (c * CW + cwave) * kWave;
       const uint8_t* ws = wbase + static_cast<int64_t>(p) * (PB * kBlockBytes);
-      if (i0 < G::wpos && i0 + lane < G::wpos) dma16_sbase(wsrc[c], ws, sb + i0 * 16);
+      if (i0 < wpos && i0 + lane < wpos) dma16_sbase(wsrc[c], ws, sb + i0 * 16);
     } else {
       constexpr int q = c - G::niw;
       const int i0 = (q * CW + cwave) * kWave;
@@ -296,7 +310,7 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
     for (int w = 0; w < NW; ++w) sum += q[w * kWave * 4];
     sum *= 0x1p24f;  // exact rescale of the subnormal code products
     const int64_t row = row0 + 16 * i + wr;
-    if (row < n) {
+    if (16 * i + wr < rv) {
       const int64_t off = static_cast<int64_t>(ar) * n + row;
       if (y_f16) static_cast<half_t*>(y)[off] = static_cast<half_t>(sum);
       else static_cast<float*>(y)[off] = sum;
@@ -304,14 +318,12 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
   }
 }
 
-constexpr int kTLdsMax = 160 * 1024;
-
-template <int T, int AT, int PB, int NW = 8, int NP = 4>
-hipError_t launch_tile_t(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
-                         int64_t n, int64_t k, hipStream_t s) {
+template <int T, int AT, int PB, bool FULL, int NW = 8, int NP = 4>
+hipError_t launch_tile_f(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
+                         int64_t n, int64_t k, int rows, hipStream_t s) {
   using G = TileGeo<T, AT, PB, NW, NP>;
   static_assert(G::lds <= kTLdsMax, "LDS budget");
-  const void* fn = reinterpret_cast<const void*>(&gemv_tile_kernel<T, AT, PB, NW, NP>);
+  const void* fn = reinterpret_cast<const void*>(&gemv_tile_kernel<T, AT, PB, FULL, NW, NP>);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     const hipError_t e =
@@ -319,34 +331,50 @@ hipError_t launch_tile_t(const void* x, const uint8_t* packed, void* y, bool y_f
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t grid = (n + 16 * T - 1) / (16 * T);
+  if (rows < 1 || rows > 16 * T) return hipErrorInvalidValue;
+  const int64_t grid = (n + rows - 1) / rows;
   const half_t* xp = static_cast<const half_t*>(x);
   int yf = y_f16 ? 1 : 0;
-  void* argv[] = {&xp, const_cast<const uint8_t**>(&packed), &y, &m, &n, &k, &yf};
+  void* argv[] = {&xp, const_cast<const uint8_t**>(&packed), &y, &m, &n, &k, &yf, &rows};
   return hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(G::lanes), argv,
                          static_cast<size_t>(G::lds), s);
 }
 
+template <int T, int AT, int PB>
+hipError_t launch_tile_t(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
+                         int64_t n, int64_t k, int rows, hipStream_t s) {
+  if (rows == 16 * T) return launch_tile_f<T, AT, PB, true>(x, packed, y, y_f16, m, n, k, rows, s);
+  return launch_tile_f<T, AT, PB, false>(x, packed, y, y_f16, m, n, k, rows, s);
+}
+
 struct TilePlan {
-  int T, AT, PB;
+  int T, AT, PB, rows;
 };
 
-// Row tiles per workgroup: enough for one workgroup per compute unit, capped
-// where the LDS ring would not fit (larger matrices take several rounds).
+// Rows per workgroup: whole 16-row tiles, enough for one workgroup per
+// compute unit (capped where the LDS ring would not fit; larger matrices take
+// several rounds).  With K long enough for eight or more phases the rows are
+// instead spread evenly over every compute unit (the last tile partial): the
+// streamed bytes per compute unit then dominate, and spreading lowers them.
+// With fewer phases the extra workgroups' activation traffic and start-up
+// cost more than that saves (measured at 5120 x 5120, m = 10 and 16).
 TilePlan tile_plan(int m, int64_t n, int64_t k) {
-  const int64_t tiles = (n + 15) / 16;
   const int64_t cu = device_cu_count();
-  int64_t t = (tiles + cu - 1) / cu;
-  if (t < 1) t = 1;
   TilePlan p;
   p.AT = m > 16 ? 2 : 1;
-  if (p.AT == 1 && t <= 2 && k % 1024 == 0) {
-    p.T = static_cast<int>(t);
-    p.PB = 32;
-  } else {
-    p.T = static_cast<int>(t > (p.AT == 1 ? 5 : 4) ? (p.AT == 1 ? 5 : 4) : t);
-    p.PB = 16;
+  const int tmax = p.AT == 1 ? 5 : 4;
+  int64_t tfull = ((n + 15) / 16 + cu - 1) / cu;
+  if (tfull < 1) tfull = 1;
+  if (tfull > tmax) tfull = tmax;
+  p.PB = p.AT == 1 && tfull <= 2 && k % 1024 == 0 ? 32 : 16;
+  int64_t rows = 16 * tfull;
+  const int64_t nph = k / (p.PB * kQK);
+  if (nph >= 8) {
+    const int64_t spread = (n + cu - 1) / cu;
+    if (spread < rows) rows = spread;
   }
+  p.rows = static_cast<int>(rows);
+  p.T = static_cast<int>((rows + 15) / 16);
   return p;
 }
 
@@ -354,12 +382,12 @@ template <int AT, int PB>
 hipError_t launch_tile_tt(const TilePlan& p, const void* x, const uint8_t* packed, void* y,
                           bool y_f16, int m, int64_t n, int64_t k, hipStream_t s) {
   switch (p.T) {
-    case 1: return launch_tile_t<1, AT, PB>(x, packed, y, y_f16, m, n, k, s);
-    case 2: return launch_tile_t<2, AT, PB>(x, packed, y, y_f16, m, n, k, s);
-    case 3: return launch_tile_t<3, AT, PB>(x, packed, y, y_f16, m, n, k, s);
-    case 4: return launch_tile_t<4, AT, PB>(x, packed, y, y_f16, m, n, k, s);
+    case 1: return launch_tile_t<1, AT, PB>(x, packed, y, y_f16, m, n, k, p.rows, s);
+    case 2: return launch_tile_t<2, AT, PB>(x, packed, y, y_f16, m, n, k, p.rows, s);
+    case 3: return launch_tile_t<3, AT, PB>(x, packed, y, y_f16, m, n, k, p.rows, s);
+    case 4: return launch_tile_t<4, AT, PB>(x, packed, y, y_f16, m, n, k, p.rows, s);
     default:
-      if constexpr (AT == 1 && PB == 16) return launch_tile_t<5, AT, PB>(x, packed, y, y_f16, m, n, k, s);
+      if constexpr (AT == 1 && PB == 16) return launch_tile_t<5, AT, PB>(x, packed, y, y_f16, m, n, k, p.rows, s);
       return hipErrorInvalidValue;
   }
 }
@@ -373,8 +401,8 @@ hipError_t launch_gemv_tile(const void* x, const uint8_t* packed, void* y, bool 
   const TilePlan p = tile_plan(m, n, k);
   if (p.AT == 2) return launch_tile_tt<2, 16>(p, x, packed, y, y_f16, m, n, k, s);
   if (p.PB == 32) {
-    if (p.T == 1) return launch_tile_t<1, 1, 32>(x, packed, y, y_f16, m, n, k, s);
-    return launch_tile_t<2, 1, 32>(x, packed, y, y_f16, m, n, k, s);
+    if (p.T == 1) return launch_tile_t<1, 1, 32>(x, packed, y, y_f16, m, n, k, p.rows, s);
+    return launch_tile_t<2, 1, 32>(x, packed, y, y_f16, m, n, k, p.rows, s);
   }
   return launch_tile_tt<1, 16>(p, x, packed, y, y_f16, m, n, k, s);
 }

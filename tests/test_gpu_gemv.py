@@ -188,3 +188,16 @@ def test_matrix_core_tile_shapes(q4lib, gpu, m, n, k):
     packed = oracle.quantize(w)
     g = run_gemv(q4lib, x, packed, n, k, "f16", gpu)
     assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")
+
+
+@pytest.mark.parametrize("m", [5, 16, 17, 32])
+@pytest.mark.parametrize("n,k", [(4097, 8192), (1000, 16384)])
+def test_matrix_core_tile_rows_spread(q4lib, gpu, m, n, k):
+    """K long enough for eight or more phases: rows spread over every compute
+    unit, 17 (4097 rows) or 4 (1000 rows) per workgroup, so every workgroup's
+    last 16-row tile is partial and its unfilled rows must never be stored."""
+    w = synth.random_weights(17 * m + n + k, n, k, "student_t")
+    x = synth.random_activations(19 * m + k, m, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemv(q4lib, x, packed, n, k, "f32", gpu)
+    assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")
