@@ -10,16 +10,21 @@
 //
 // Mapping: eight lanes per block, lane p holds elements 4p..4p+3, so a wave
 // reads 64 x 16 contiguous bytes (fp32) per load instruction.  The block
-// maximum is a 3-step xor-shuffle reduction inside each group of eight; the
-// high-nibble codes of elements 16..31 (lanes 4..7) are shuffled down onto
-// lanes 0..3, which then own four finished code bytes each.  The kernel is
-// HBM-bound: it reads 4 (fp32) or 2 (fp16) bytes and writes 0.5625 bytes per
-// weight.  Division is the IEEE-correct fp32 division: the library is built
-// without fast-math.
+// maximum is a 3-step DPP reduction inside each group of eight; the
+// high-nibble codes of elements 16..31 (lanes 4..7) are moved down onto
+// lanes 0..3, which then own four finished code bytes each.  The kernel
+// reads 4 (fp32) or 2 (fp16) bytes and writes 0.5625 bytes per weight.  The
+// codes follow the correctly rounded fp32 division exactly: a reciprocal with
+// one residual step decides every code whose t is not within 2^-16 of an
+// integer, the rest redo the IEEE division (the library is built without
+// fast-math).
 #include "q4_internal.hpp"
 
 namespace q4 {
 namespace {
+
+constexpr int kQuantUF32 = 4;  // blocks in flight per lane group (16-byte loads)
+constexpr int kQuantUF16 = 8;  // (8-byte loads)
 
 template <typename T>
 struct Load4;
@@ -41,19 +46,54 @@ struct Load4<half_t> {
   }
 };
 
-template <typename T>
-__global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ w,
-                                                       uint8_t* __restrict__ out,
-                                                       int64_t nblocks) {
-  const int part = threadIdx.x & 7;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 3);
-  // Grid-stride over blocks; the eight lanes of a group always share `blk`,
-  // so they enter and leave the loop together.
-  for (int64_t blk = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 3;
-       blk < nblocks; blk += stride) {
-  float v[4];
-  Load4<T>::run(w + blk * kQK + part * 4, v);
+// Lane exchange inside a group of eight (DPP, no LDS round trip).
+constexpr int kDppXor1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppShl4 = 0x104;     // lane i reads lane i + 4 (row_shl:4)
 
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+
+// Keep the (value, index) of larger magnitude, the smaller index on a tie.
+template <int CTRL>
+__device__ __forceinline__ void amax_step(float& best, float& bmag, int& bidx) {
+  const float ob = dpp_f<CTRL>(best);
+  const int oi = dpp_i<CTRL>(bidx);
+  const float om = fabsf(ob);
+  if (om > bmag || (om == bmag && oi < bidx)) { best = ob; bmag = om; bidx = oi; }
+}
+
+// Code q = min(15, trunc(fl(fl(x / D) + 8.5))) (negative truncations clamp to
+// 0).  Fast path: r ~ 1/D (v_rcp_f32, 1 ulp), u = x r refined by one
+// residual step e = fma(-u, D, x), u += e r, which leaves u within 2 ulp of
+// the correctly rounded quotient (|u| <= 12 here, so 2^-19), and t = u + 8.5
+// within 2^-18 of the rule's t.  Only a t within 2^-16 of an integer can
+// truncate differently; those lanes redo the correctly rounded division.
+__device__ __forceinline__ int code_of(float x, float D, float r) {
+  float u = x * r;
+  const float e = fmaf(-u, D, x);
+  u = fmaf(e, r, u);
+  float t = u + 8.5f;
+  if (fabsf(t - __builtin_rintf(t)) < 0x1p-16f) {
+    const float ue = x / D;
+    asm volatile("" : "+v"(t));
+    t = ue + 8.5f;
+  }
+  const int q = static_cast<int>(t);  // truncation
+  return q < 0 ? 0 : (q > 15 ? 15 : q);
+}
+
+// One block: the eight lanes of a group share `blk` and hold its elements
+// 4p .. 4p + 3 in v.
+__device__ __forceinline__ void quantize_block(int64_t blk, int part, const float (&v)[4],
+                                               uint8_t* __restrict__ out) {
   // Largest magnitude inside this lane, first index on ties.
   float best = v[0];
   float bmag = fabsf(v[0]);
@@ -63,15 +103,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ w,
     const float a = fabsf(v[i]);
     if (a > bmag) { bmag = a; best = v[i]; bidx = part * 4 + i; }
   }
-  // Across the eight lanes of the block; the combine is symmetric so every
-  // lane ends with the same (value, index).
-#pragma unroll
-  for (int off = 1; off < 8; off <<= 1) {
-    const float ob = __shfl_xor(best, off, 8);
-    const int oi = __shfl_xor(bidx, off, 8);
-    const float om = fabsf(ob);
-    if (om > bmag || (om == bmag && oi < bidx)) { best = ob; bmag = om; bidx = oi; }
-  }
+  // Across the eight lanes: both quads, then the other quad (the mirror pairs
+  // lanes whose quads already agree), so every lane ends with the same pair.
+  amax_step<kDppXor1>(best, bmag, bidx);
+  amax_step<kDppXor2>(best, bmag, bidx);
+  amax_step<kDppHalfMirror>(best, bmag, bidx);
 
   // The quotient is exact in fp32 (a power-of-two scaling), then rounded once
   // to fp16.  The empty asm keeps the compiler from fusing the two steps into a
@@ -82,21 +118,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ w,
   const half_t dh = static_cast<half_t>(t);
   const float D = static_cast<float>(dh);
 
-  uint32_t nib = 0;
+  uint32_t nib = 0x08080808u;  // every q is 8 when d is zero
+  if (D != 0.0f) {
+    const float r = __builtin_amdgcn_rcpf(D);
+    nib = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int q = 8;
-    if (D != 0.0f) {
-      const float u = v[i] / D;
-      const float t = u + 8.5f;
-      q = static_cast<int>(truncf(t));
-      q = q < 0 ? 0 : (q > 15 ? 15 : q);
-    }
-    nib |= static_cast<uint32_t>(q) << (8 * i);
+    for (int i = 0; i < 4; ++i) nib |= static_cast<uint32_t>(code_of(v[i], D, r)) << (8 * i);
   }
   // Lane p (< 4) holds low nibbles of code bytes 4p..4p+3; lane p+4 holds the
   // matching high nibbles (elements 16 + 4p ..).
-  const uint32_t hi = __shfl_down(nib, 4, 8);
+  const uint32_t hi = static_cast<uint32_t>(dpp_i<kDppShl4>(static_cast<int>(nib)));
   uint8_t* ob = out + blk * kBlockBytes;
   if (part < 4) {
     const uint32_t bytes = nib | (hi << 4);
@@ -107,6 +138,33 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ w,
   if (part == 0) {
     *reinterpret_cast<uint16_t*>(ob) = __builtin_bit_cast(uint16_t, dh);
   }
+}
+
+// Each group of eight lanes takes U blocks per sweep, blk0 + u * stride, and
+// issues all U loads before quantising any: one load in flight per lane would
+// leave about 32 KB in flight per CU, which at HBM latency caps the stream
+// near 4 TB/s.
+template <typename T, int U>
+__global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ w,
+                                                       uint8_t* __restrict__ out,
+                                                       int64_t nblocks) {
+  const int part = threadIdx.x & 7;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 3);
+  // The eight lanes of a group always share their blocks, so they take every
+  // branch together (the shuffles stay within active groups).
+  for (int64_t blk0 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 3;
+       blk0 < nblocks; blk0 += U * stride) {
+    float v[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t blk = blk0 + u * stride;
+      if (blk < nblocks) Load4<T>::run(w + blk * kQK + part * 4, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t blk = blk0 + u * stride;
+      if (blk < nblocks) quantize_block(blk, part, v[u], out);
+    }
   }
 }
 
@@ -115,18 +173,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ w,
 hipError_t launch_quantize(const void* w, DType wt, int64_t n, int64_t k,
                            uint8_t* packed, hipStream_t s) {
   const int64_t nblocks = n * (k / kQK);
-  const int64_t groups = (nblocks * 8 + 255) / 256;
-  const dim3 grid(static_cast<unsigned>(groups < 65536 ? groups : 65536));
+  const int U = wt == DType::F32 ? kQuantUF32 : kQuantUF16;
+  const int64_t groups = (nblocks + 32 * U - 1) / (32 * U);  // 32 blocks per workgroup per sweep
+  const dim3 grid(static_cast<unsigned>(groups < 65535 ? groups : 65535));
   const dim3 block(256);
   if (wt == DType::F32) {
     const float* p = static_cast<const float*>(w);
     void* argv[] = {&p, &packed, const_cast<int64_t*>(&nblocks)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&quantize_kernel<float>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&quantize_kernel<float, kQuantUF32>),
                            grid, block, argv, 0, s);
   }
   const half_t* p = static_cast<const half_t*>(w);
   void* argv[] = {&p, &packed, const_cast<int64_t*>(&nblocks)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&quantize_kernel<half_t>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&quantize_kernel<half_t, kQuantUF16>),
                          grid, block, argv, 0, s);
 }
 

@@ -71,3 +71,29 @@ def test_deterministic(q4lib, gpu):
     a = to_host(q4lib.q4_quantize(w))
     b = to_host(q4lib.q4_quantize(w))
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_codes_at_rounding_boundaries(q4lib, gpu, dt):
+    """Elements within a few ulps of the points where x / d + 8.5 crosses an
+    integer (x / d = j + 1/2), for scales across the fp16 range: the code then
+    depends on the correctly rounded quotient and on the rounded addition, so
+    any quotient that is merely close would change some of these bytes."""
+    rng = np.random.default_rng(11)
+    nblk = 4096
+    # scales: random fp16 values, normal and subnormal
+    e = rng.integers(-24, 12, nblk)
+    d = (rng.integers(1024, 2048, nblk).astype(np.float64) * 2.0 ** (e - 10)).astype(np.float16)
+    d = np.where(d == 0, np.float16(2.0 ** -24), d).astype(np.float32)
+    j = rng.integers(-8, 8, (nblk, 32)).astype(np.float64) + 0.5
+    ulps = rng.integers(-3, 4, (nblk, 32)).astype(np.float64)
+    x = (j * d[:, None] * (1.0 + ulps * 2.0 ** -24)).astype(np.float32)
+    x[:, 0] = -8.0 * d  # pins the scale: m / -8 = d exactly
+    if dt == "f16":
+        x = x.astype(np.float16)
+        x[:, 0] = (-8.0 * d).astype(np.float16)
+    w = x.reshape(64, 64 * 32)
+    got = gpu_quantize(q4lib, w, gpu)
+    want = oracle.quantize(w)
+    bad = np.nonzero(np.any(got.reshape(-1, 18) != want.reshape(-1, 18), axis=1))[0]
+    assert bad.size == 0, f"{bad.size} blocks differ, first {bad[:5]}"
