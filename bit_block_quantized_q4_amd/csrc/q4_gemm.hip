@@ -439,10 +439,11 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
 // wave order at the end.
 //
 // Copies (global -> LDS, 16-byte pieces, issued by all waves):
-//   - activations: a ring of four 64-wide k stages, stage s of step ks = ks % 4,
-//     refilled four steps ahead;
+//   - activations: a ring of six 64-wide k stages, stage of step ks = ks % 6,
+//     refilled five steps ahead;
 //   - packed weights: the 144 bytes of each row that cover four steps (256 k,
-//     16-byte aligned because k % 256 == 0), a ring of two.
+//     16-byte aligned because k % 256 == 0), a ring of three, refilled three
+//     segments ahead.
 // Per step: issue copies, read the next step's activation fragments and the
 // raw weights of the step after, run this step's 16 matrix products
 // interleaved with those reads and with the dequantisation of the next
@@ -452,8 +453,9 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
 constexpr int kSkAStage = 128 * kRowBytes16;        // 16 KB
 constexpr int kSkSeg = 4 * 2 * kBlockBytes;         // 144 packed bytes per row and 4 steps
 constexpr int kSkWStage = 128 * kSkSeg;             // 18 KB
-constexpr int kSkWOff = 4 * kSkAStage;              // weight ring after the activation ring
-constexpr int kSkLds = kSkWOff + 2 * kSkWStage;     // 100 KB
+constexpr int kSkAStages = 6;
+constexpr int kSkWOff = kSkAStages * kSkAStage;     // weight ring after the activation ring
+constexpr int kSkLds = kSkWOff + 3 * kSkWStage;     // 150 KB
 constexpr int kSkRedCol = 36;                       // floats per column of a partial (32 rows + pad)
 static_assert(4 * 128 * kSkRedCol * 4 <= kSkLds, "reduction buffer");
 
@@ -479,41 +481,46 @@ __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
   W += static_cast<int64_t>(ks0) * 2 * kBlockBytes;
   y += static_cast<int64_t>(blockIdx.z) * zstride;
 
+  // Copies take a wave-uniform base (the tile's first row at step ks, or its
+  // first weight row at segment ss) plus a 32-bit per-lane byte offset.
   // Activation copy i of this thread: LDS piece P = 256 i + tid of a stage
   // (row P / 8, swizzled column P % 8).
-  const half_t* asrc[4];
+  const uint32_t lds0 = lds_addr(smem);
+  uint32_t aoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int P = 256 * i + tid;
     const int r = P >> 3;
     const int c = (P & 7) ^ (r & 7);
-    const int64_t row = m0 + r < m ? m0 + r : m - 1;
-    asrc[i] = x + row * k + 8 * c;
+    const int64_t rr = m0 + r < m ? r : m - 1 - m0;
+    aoff[i] = static_cast<uint32_t>((rr * k + 8 * c) * 2);
   }
+  const half_t* const xt = x + m0 * k;
   auto issue_a = [&](int ks, int stage) {
-    uint8_t* dst = smem + stage * kSkAStage;
+    const half_t* base = xt + static_cast<int64_t>(ks) * kBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      dma16(asrc[i] + static_cast<int64_t>(ks) * kBK, dst + (256 * i + 64 * wave) * 16);
+      dma16_sbase(aoff[i], base, lds0 + stage * kSkAStage + (256 * i + 64 * wave) * 16);
   };
   // Weight copy i of this thread: piece p of a weight stage (row p / 9, piece
   // p % 9 of its 144 bytes); 1152 pieces = four full rounds of 256 plus a
   // fifth in which each wave copies 32.
-  const uint8_t* wsrc[5];
+  uint32_t woff[5];
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
     const int p = i < 4 ? 256 * i + tid : 1024 + 32 * wave + lc;
     const int r = p / 9;
     const int c = p - 9 * r;
-    const int64_t row = n0 + r < n ? n0 + r : n - 1;
-    wsrc[i] = W + row * rb + 16 * c;
+    const int64_t rr = n0 + r < n ? r : n - 1 - n0;
+    woff[i] = static_cast<uint32_t>(rr * rb + 16 * c);
   }
+  const uint8_t* const wt = W + n0 * rb;
   auto issue_w = [&](int ss, int buf) {
-    uint8_t* dst = smem + kSkWOff + buf * kSkWStage;
-    const int64_t off = static_cast<int64_t>(ss) * kSkSeg;
+    const uint8_t* base = wt + static_cast<int64_t>(ss) * kSkSeg;
+    const uint32_t dst = lds0 + kSkWOff + buf * kSkWStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + off, dst + (256 * i + 64 * wave) * 16);
-    if (lane < 32) dma16(wsrc[4] + off, dst + (1024 + 32 * wave) * 16);
+    for (int i = 0; i < 4; ++i) dma16_sbase(woff[i], base, dst + (256 * i + 64 * wave) * 16);
+    if (lane < 32) dma16_sbase(woff[4], base, dst + (1024 + 32 * wave) * 16);
   };
 
   // This wave's share of a step: block b = w >> 1 of the step and its code
@@ -541,18 +548,22 @@ __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
     uint32_t w[4][3];
     uint32_t d[4];
   };
-  // Reads past the last step are of valid LDS addresses and unused.
-  auto read_a = [&](int ks, half8_t (&fa)[4]) {
-    const uint8_t* as = smem + (ks & 3) * kSkAStage;
+  // Fragment reads from a lane base plus compile-time offsets (stage, buffer,
+  // step within the segment, fragment).  Reads past the last step are of
+  // valid LDS addresses and unused.
+  const uint8_t* const abase = smem + lc * 128 + 16 * (apiece ^ (lc & 7));  // swz(32 i + lc, apiece)
+  const uint8_t* const wbase = smem + kSkWOff + lc * kSkSeg + 16 * b;
+  auto read_a = [&](auto stage_c, half8_t (&fa)[4]) {
+    constexpr int stage = decltype(stage_c)::value;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      fa[i] = *reinterpret_cast<const half8_t*>(as + swz(32 * i + lc, apiece) * 16);
+      fa[i] = *reinterpret_cast<const half8_t*>(abase + stage * kSkAStage + i * 4096);
   };
-  auto read_w = [&](int ks, Raw& raw) {
-    const uint8_t* ws = smem + kSkWOff + ((ks >> 2) & 1) * kSkWStage + 36 * (ks & 3) + 16 * b;
+  auto read_w = [&](const uint8_t* wb, auto j_c, Raw& raw) {
+    constexpr int off = 36 * decltype(j_c)::value;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const uint8_t* rp = ws + (32 * jj + lc) * kSkSeg;
+      const uint8_t* rp = wb + off + jj * 32 * kSkSeg;
       const uint32_t* win = reinterpret_cast<const uint32_t*>(rp + 8 * h);
       raw.w[jj][0] = win[0];
       raw.w[jj][1] = win[1];
@@ -586,78 +597,103 @@ __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Prologue: copies in the order the loop's waits assume (A0 W0 A1 A2 W1
-  // A3); once A0, W0 and A1 have landed: step 0's operands, step 1's raw
-  // weights, then a barrier before step 0 refills stage 0.
+  // Prologue: copies in the order the loop's waits assume (W0 A0 W1 A1 A2
+  // A3 A4 W2, as if steps -5 .. -1 had run); once A0, W0 and A1 have landed:
+  // step 0's operands and step 1's raw weights.
   const int last = nks - 1;
-  issue_a(0, 0);
   issue_w(0, 0);
+  issue_a(0, 0);
+  issue_w(1 < nss - 1 ? 1 : nss - 1, 1);
   issue_a(1 < last ? 1 : last, 1);
   issue_a(2 < last ? 2 : last, 2);
-  issue_w(1 < nss - 1 ? 1 : nss - 1, 1);
   issue_a(3 < last ? 3 : last, 3);
-  wait_vm_lgkm0<13>();
+  issue_a(4 < last ? 4 : last, 4);
+  issue_w(2 < nss - 1 ? 2 : nss - 1, 2);
+  wait_vm_lgkm0<17>();
   __builtin_amdgcn_s_barrier();
   compiler_fence();
   half8_t fa[4], fb[4];
   Raw rc;  // raw weights of step ks + 1
   {
     Raw r0;
-    read_a(0, fa);
-    read_w(0, r0);
-    read_w(1, rc);
+    read_a(IC<0>{}, fa);
+    read_w(wbase, IC<0>{}, r0);
+    read_w(wbase, IC<1>{}, rc);
     dequant(r0, fb);
   }
-  wait_vm_lgkm0<13>();
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
+  // (step 0 refills stage 5, which nothing has read: no barrier needed here)
 
   // Step ks = 4 ss + j works on operands in registers and, for the steps
   // ahead, reads step ks + 1's activation fragments and step ks + 2's raw
-  // weights and dequantises step ks + 1's.  Copies: A(ks + 4) into stage j
-  // (read last during step ks - 1), and at j = 2 weight stage ss + 2 into
-  // buffer ss & 1 (read last during step ks - 1).  The wait before the
-  // barrier leaves in flight only copies issued after those the next step
-  // reads: A(ks + 2), and at j = 1 also W(ss + 1).
-  for (int ss = 0; ss < nss; ++ss) {
+  // weights and dequantises step ks + 1's.  Copies: A(ks + 5) into stage
+  // (ks - 1) % 6, and at j = 3, after it, weight segment ss + 3 into buffer
+  // ss % 3.  Both were last read a step before this one and those reads were
+  // consumed (by step ks - 1's products, by this step's predecessor's
+  // dequantisation) before the last barrier, so no wave waits for its LDS
+  // reads at a barrier.  The wait is for A(ks + 2), which step ks + 1 reads:
+  // issued at step ks - 3, it has the three later activation copies and
+  // exactly one weight segment (every four steps issue one) behind it, 17
+  // copies.  Copies retire in order, so every weight segment older than it
+  // (among them the one step ks + 1 reads) has landed too; an activation
+  // copy issued right after a weight segment is due four steps later.
+  // Twelve steps (three segments) per loop trip, so that every stage and
+  // buffer index is a constant: with ss = 3 q + sr, step ks = 4 ss + j has
+  // stage (4 sr + j) % 6 and reads weight buffers sr and (sr + 1) % 3.
+  auto step = [&](auto j_c, auto sr_c, int ss) {
+    constexpr int j = decltype(j_c)::value;
+    constexpr int sr = decltype(sr_c)::value;
+    constexpr int sa = (4 * sr + j) % kSkAStages;                   // stage of step ks
+    constexpr int sn = (sa + 1) % kSkAStages;                       // of step ks + 1
+    constexpr int sp = (sa + kSkAStages - 1) % kSkAStages;          // of step ks - 1
+    constexpr int wcur = sr, wnext = (sr + 1) % 3;
+    const int ks = 4 * ss + j;
+    issue_a(ks + 5 < last ? ks + 5 : last, sp);
+    if constexpr (j == 3) issue_w(ss + 3 < nss - 1 ? ss + 3 : nss - 1, wcur);
+    half8_t na[4], nb[4];
+    Raw rn;
+    read_a(IC<sn>{}, na);
+    read_w(wbase + (j < 2 ? wcur : wnext) * kSkWStage, IC<(j + 2) & 3>{}, rn);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ks = 4 * ss + j;
-      issue_a(ks + 4 < last ? ks + 4 : last, j);
-      if (j == 2) issue_w(ss + 2 < nss - 1 ? ss + 2 : nss - 1, ss & 1);
-      half8_t na[4], nb[4];
-      Raw rn;
-      read_a(ks + 1, na);
-      read_w(ks + 2, rn);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int jj = 0; jj < 4; ++jj)
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
+    dequant(rc, nb);
+    // each product followed by one fragment read and a share of the
+    // dequantisation
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
-      dequant(rc, nb);
-      // each product followed by one fragment read and a share of the
-      // dequantisation
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        tie_after(nb[i]);  // dequantised within this step, not sunk into the next
-        fa[i] = na[i];
-        fb[i] = nb[i];
-      }
-      rc = rn;
-      __builtin_amdgcn_sched_barrier(0);
-      if (j == 1) wait_vm_lgkm0<8>();
-      else wait_vm_lgkm0<13>();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      compiler_fence();
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tie_after(nb[i]);  // dequantised within this step, not sunk into the next
+      fa[i] = na[i];
+      fb[i] = nb[i];
+    }
+    rc = rn;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<17>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    compiler_fence();
+  };
+  auto segment = [&](auto sr_c, int ss) {
+    step(IC<0>{}, sr_c, ss);
+    step(IC<1>{}, sr_c, ss);
+    step(IC<2>{}, sr_c, ss);
+    step(IC<3>{}, sr_c, ss);
+  };
+  int ss = 0;
+  for (; ss + 3 <= nss; ss += 3) {
+    segment(IC<0>{}, ss);
+    segment(IC<1>{}, ss + 1);
+    segment(IC<2>{}, ss + 2);
   }
+  if (ss < nss) segment(IC<0>{}, ss);
+  if (ss + 1 < nss) segment(IC<1>{}, ss + 1);
   wait_vm_lgkm0<0>();
   __syncthreads();
 
