@@ -415,7 +415,9 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
   }
 
   // 32x32 accumulator layout: lane l holds column l % 32; register r holds
-  // row 8 * (r / 4) + 4 * (l / 32) + r % 4.
+  // row 8 * (r / 4) + 4 * (l / 32) + r % 4.  (Storing y transposed from
+  // swapped operands, four columns per 8-byte store, measured slower: each
+  // store then touches 32 rows.)
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -699,9 +701,15 @@ __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
 
   // Sum the four partial tiles, one 32-row fragment row at a time: each wave
   // writes its partial column-major (column stride kSkRedCol floats), then
-  // thread t sums column t % 128, rows 16 (t / 128) .. + 15 in wave order.
+  // thread t sums the 4 x 4 block of rows 4 (t % 8) .. + 3 and columns
+  // 4 (t / 8) .. + 3 in wave order and stores each row's 4 columns with one
+  // 8-byte (fp16) or 16-byte (fp32) store; a store instruction costs about
+  // as much as a copy, so per-element stores made this epilogue several
+  // microseconds long.
   float* red = reinterpret_cast<float*>(smem);
-  const int scol = tid & 127, srow = 16 * (tid >> 7);
+  const int rb4 = tid & 7, cb4 = tid >> 3;
+  const int64_t col = n0 + 4 * cb4;
+  const bool vec_ok = (ldy & 3) == 0 && col + 3 < n;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -712,22 +720,33 @@ __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
         *reinterpret_cast<float4_t*>(red + (wave * 128 + 32 * jj + lc) * kSkRedCol + 8 * q + 4 * kg) = v;
       }
     __syncthreads();
-    float4_t s4[4];
+    float4_t sc[4];  // column c of the block, rows 4 rb4 .. + 3
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s4[q] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 4; ++c) sc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        s4[q] += *reinterpret_cast<const float4_t*>(red + (w * 128 + scol) * kSkRedCol + srow + 4 * q);
-    const int64_t col = n0 + scol;
+      for (int c = 0; c < 4; ++c)
+        sc[c] += *reinterpret_cast<const float4_t*>(red + (w * 128 + 4 * cb4 + c) * kSkRedCol + 4 * rb4);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = m0 + 32 * i + 4 * rb4 + r;
+      if (row >= m) continue;
+      YT* dst = y + row * ldy + col;
+      if (vec_ok) {
+        if constexpr (sizeof(YT) == 2) {
+          const half4_t h = {static_cast<half_t>(sc[0][r]), static_cast<half_t>(sc[1][r]),
+                             static_cast<half_t>(sc[2][r]), static_cast<half_t>(sc[3][r])};
+          *reinterpret_cast<half4_t*>(dst) = h;
+        } else {
+          *reinterpret_cast<float4_t*>(dst) = float4_t{sc[0][r], sc[1][r], sc[2][r], sc[3][r]};
+        }
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t row = m0 + 32 * i + srow + 4 * q + e;
-        if (row < m && col < n) y[row * ldy + col] = static_cast<YT>(s4[q][e]);
+        for (int c = 0; c < 4; ++c)
+          if (col + c < n) dst[c] = static_cast<YT>(sc[c][r]);
       }
+    }
     __syncthreads();
   }
 }
