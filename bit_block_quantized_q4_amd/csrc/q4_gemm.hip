@@ -795,13 +795,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 // Launch plan: main tiles (256 x 256 with 8 waves for m >= 1024, else
 // 128 x 128 with 4: slice-K when k % 256 == 0 and k >= 1024) over the
-// leading n_main columns in whole rounds of one tile per compute unit.  When a partial round would be left, the remaining
-// columns use the same tiles with K split `splits` ways so that the tail fills
-// the compute units; the fp32 partials go to the workspace and one reduction
-// sums them in split order.
+// leading n_main columns in whole rounds of one tile per compute unit.  When
+// a partial round would be left, the remaining columns run with K split
+// `splits` ways so that the tail fills the compute units (slice-K tiles when
+// k allows, else the main tiles); the fp32 partials go to the workspace and
+// one reduction sums them in split order.
 struct GemmPlan {
   bool big = false;
-  bool slicek = false;  // 128 x 128 slice-K tiles (k % 256 == 0)
+  bool slicek = false;       // 128 x 128 slice-K main tiles (k % 256 == 0)
+  bool tail_slicek = false;  // the split-K tail runs slice-K tiles
   int64_t n_main = 0;
   int splits = 1, kps = 0;
   size_t ws_bytes = 0;
@@ -810,7 +812,8 @@ struct GemmPlan {
 GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
   GemmPlan p;
   p.big = m >= 1024;
-  p.slicek = !p.big && k % 256 == 0 && k >= 1024;  // short k: prologue and reduction dominate
+  const bool sk_ok = k % 256 == 0 && k >= 1024;  // short k: prologue and reduction dominate
+  p.slicek = !p.big && sk_ok;
   const int bm = p.big ? 256 : 128, bn = p.big ? 256 : 128;
   const int64_t cu = device_cu_count();
   const int64_t tm = (m + bm - 1) / bm, tn = (n + bn - 1) / bn;
@@ -821,12 +824,19 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
   const int64_t tn_main = (tm * tn / cu) * cu / tm;  // column tiles in whole rounds
   if (tn_main < 1 || tn_main >= tn) return p;
   const int64_t nt = n - tn_main * bn;
-  const int64_t tail_tiles = tm * ((nt + bn - 1) / bn);
+  // The tail runs slice-K 128 x 128 tiles when k allows and they still take
+  // at least two K splits: behind 256 x 256 main tiles that is four times the
+  // tiles, so fewer splits (less fp32 partial traffic) fill the compute
+  // units, and its epilogue stores four columns at a time.
+  const int64_t sk_tiles = ((m + 127) / 128) * ((nt + 127) / 128);
+  p.tail_slicek = sk_ok && cu / sk_tiles >= 2;
+  const int tb = p.tail_slicek ? 128 : bm;
+  const int64_t tail_tiles = ((m + tb - 1) / tb) * ((nt + tb - 1) / tb);
   int64_t splits = cu / tail_tiles;
   if (splits > nks) splits = nks;
   if (splits < 2) return p;
   int kps = static_cast<int>((nks + splits - 1) / splits);
-  if (p.slicek) kps = (kps + 3) / 4 * 4;  // whole 4-step weight segments
+  if (p.tail_slicek) kps = (kps + 3) / 4 * 4;  // whole 4-step weight segments
   p.n_main = tn_main * bn;
   p.kps = kps;
   p.splits = (nks + kps - 1) / kps;
@@ -846,12 +856,12 @@ hipError_t dispatch_tiled(const half_t* x, const uint8_t* packed, YT* y, int64_t
   // Tail: split z of K writes part[z], m x nt with row stride nt.
   const int64_t nt = n - p.n_main;
   float* part = static_cast<float*>(workspace);
-  e = p.big      ? launch_tiled<256, 256, 2, 4, float>(x, packed, p.n_main, nt, part, m, k, nt,
-                                                      p.splits, p.kps, m * nt, s)
-      : p.slicek ? launch_slicek<float>(x, packed, p.n_main, nt, part, m, k, nt, p.splits, p.kps,
-                                        m * nt, s)
-                 : launch_tiled<128, 128, 2, 2, float>(x, packed, p.n_main, nt, part, m, k, nt,
-                                                      p.splits, p.kps, m * nt, s);
+  e = p.tail_slicek ? launch_slicek<float>(x, packed, p.n_main, nt, part, m, k, nt, p.splits,
+                                            p.kps, m * nt, s)
+      : p.big        ? launch_tiled<256, 256, 2, 4, float>(x, packed, p.n_main, nt, part, m, k, nt,
+                                                          p.splits, p.kps, m * nt, s)
+                     : launch_tiled<128, 128, 2, 2, float>(x, packed, p.n_main, nt, part, m, k, nt,
+                                                          p.splits, p.kps, m * nt, s);
   if (e != hipSuccess) return e;
   const int64_t quads = m * nt / 4;
   YT* yt = y + p.n_main;

@@ -152,12 +152,13 @@ def test_graph_replay_matches_eager(q4lib, gpu):
 
 
 @pytest.mark.parametrize("m,n,k", [(300, 11000, 256), (1100, 14000, 128), (256, 17408, 512),
-                                   (2048, 17408, 64)])
+                                   (2048, 17408, 64), (1030, 13200, 1024)])
 def test_main_and_tail_launches(q4lib, gpu, m, n, k):
     """Shapes whose tile count leaves a partial round on 256 compute units: the
-    leading columns go to the main tiles in whole rounds, the rest to the same
-    tiles with K split across workgroups (fp32 partials in the workspace, then
-    a fixed-order reduction); every output is checked."""
+    leading columns go to the main tiles in whole rounds, the rest to tiles
+    with K split across workgroups (fp32 partials in the workspace, then a
+    fixed-order reduction); 1030 x 13200 x 1024 puts slice-K tail tiles
+    behind 256 x 256 main tiles.  Every output is checked."""
     w = synth.random_weights(3 * m + n + k, n, k, "student_t")
     x = synth.random_activations(7 * m + k, m, k, "f16")
     packed = oracle.quantize(w)
