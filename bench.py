@@ -17,6 +17,9 @@ The same JSON line carries:
   gemm          -- prefill GEMM on the 2048 x 17408 x 5120 workload, whole
                    batch and 8 chunks of 256 rows, TFLOP/s against fp16 MFMA;
   quantize      -- the quantiser on the same 5120 x 5120 fp32 weight;
+  layer_decode  -- one 27B-class layer's seven decode linears at M = 1 and 10,
+                   as seven launches and as four (q/k/v and gate/up each one
+                   launch on their concatenated packed rows);
   cpu_baseline  -- the CPU oracle timed on a bounded sample of the step.
 
 Counter passes (HBM traffic): run `bench.py --traffic` once under
@@ -226,6 +229,74 @@ def bench_gemm(q4, torch, dev, reps):
     }
 
 
+def bench_layer_decode(q4, torch, dev, steps, rotate_bytes, ms=(1, 10)):
+    """Decode through one 27B-class layer's seven linears (q, k, v, o, gate,
+    up, down) at M = 1 and 10: seven launches, against four where q/k/v and
+    gate/up run as one launch each on their packed rows concatenated (packed
+    rows are independent, so a concatenated buffer is simply a taller weight).
+    Each linear's packed copy is a row slice of its group's buffer, so both
+    variants stream the same bytes; layer copies are rotated over >= 1 GiB."""
+    import synth
+    lins = {l.name: l for l in synth.WORKLOADS[5].linears}
+    k_model = lins["q"].k
+    groups = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gateup", ["gate", "up"]), ("down", ["down"])]
+    layer_bytes = sum(l.n * (l.k // QK) * BLOCK_BYTES for l in lins.values())
+    copies = max(2, -(-rotate_bytes // layer_bytes))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    layers = []
+    for _ in range(copies):
+        bufs, views = {}, {}
+        for gname, names in groups:
+            kk = lins[names[0]].k
+            rows = sum(lins[nm].n for nm in names)
+            buf = torch.empty((rows, (kk // QK) * BLOCK_BYTES), dtype=torch.uint8, device=dev)
+            r = 0
+            for nm in names:
+                n = lins[nm].n
+                w = torch.randn((n, kk), device=dev, generator=gen) * 0.02
+                views[nm] = buf[r:r + n]
+                q4.q4_quantize(w, packed=views[nm])
+                r += n
+            bufs[gname] = buf
+        layers.append((bufs, views))
+    torch.cuda.synchronize()
+    res = {}
+    for m in ms:
+        x = torch.randn((m, k_model), device=dev, generator=gen).half()
+        xd = torch.randn((m, lins["down"].k), device=dev, generator=gen).half()
+        ysep = {nm: torch.empty((m, l.n), dtype=torch.float16, device=dev) for nm, l in lins.items()}
+        ygrp = {g: torch.empty((m, sum(lins[nm].n for nm in names)), dtype=torch.float16, device=dev)
+                for g, names in groups}
+
+        def separate():
+            for i in range(steps):
+                _, views = layers[i % copies]
+                for nm in ("q", "k", "v", "o", "gate", "up"):
+                    q4.q4_gemv(x, views[nm], y=ysep[nm])
+                q4.q4_gemv(xd, views["down"], y=ysep["down"])
+
+        def fused():
+            for i in range(steps):
+                bufs, _ = layers[i % copies]
+                for g in ("qkv", "o", "gateup"):
+                    q4.q4_gemv(x, bufs[g], y=ygrp[g])
+                q4.q4_gemv(xd, bufs["down"], y=ygrp["down"])
+
+        row = {}
+        for name, fn, launches in (("separate", separate, 7), ("fused", fused, 4)):
+            g = capture(torch, fn)
+            g.replay()
+            t = replay_seconds(torch, g) / steps
+            del g
+            row[name] = {"launches": launches, "us_per_layer": t * 1e6,
+                         "weight_gbs": layer_bytes / t / 1e9,
+                         "frac_hbm": layer_bytes / t / 1e9 / HBM_PEAK_GBS}
+        res[f"m{m}"] = row
+    return {"workload": "decode_layer_27b_dense (q,k,v,o,gate,up,down)", "weight_bytes": layer_bytes,
+            "layer_copies_rotated": copies, **res}
+
+
 # ------------------------------------------------------------ HBM traffic
 
 TRAFFIC_CALIB_BYTES = 512 << 20
@@ -394,7 +465,7 @@ def main():
     ap.add_argument("--rotate-mib", type=int, default=1024)
     ap.add_argument("--gemm-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "gemv", "gemm", "quantize"], default="all")
+    ap.add_argument("--only", choices=["all", "gemv", "gemm", "quantize", "layer"], default="all")
     ap.add_argument("--traffic", action="store_true",
                     help="run the launches the FETCH_SIZE / WRITE_SIZE counter passes read")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -452,6 +523,8 @@ def main():
         out["quantize"] = bench_quantize(q4, torch, dev, g["w_host"], 20, rotate)
     if args.only in ("all", "gemm"):
         out["gemm"] = bench_gemm(q4, torch, dev, args.gemm_reps)
+    if args.only in ("all", "layer"):
+        out["layer_decode"] = bench_layer_decode(q4, torch, dev, min(args.steps, 50), rotate)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(g["w_host"], g["n"], g["k"], g["ms"])
     out["kernel_source_hash"] = kernel_source_hash()

@@ -113,6 +113,41 @@ def test_layer_workload_sampled(q4lib, gpu):
                                 what=f"layer/{lin.name} m{m}")
 
 
+@pytest.mark.parametrize("group", [("q", "k", "v"), ("gate", "up")])
+def test_layer_concatenated_projections(q4lib, gpu, group):
+    """Linears that read the same activation run as one launch over their packed
+    rows stacked (q/k/v: 7168 rows, gate/up: 34816): each weight is quantised
+    into its row slice of one buffer, the slices match the oracle's bytes, and
+    the one GEMV over the whole buffer is within tolerance of the oracle on
+    sampled columns that include both sides of every segment boundary."""
+    import torch
+    wl = synth.WORKLOADS[5]
+    lins = [next(l for l in wl.linears if l.name == nm) for nm in group]
+    k = lins[0].k
+    assert all(l.k == k for l in lins)
+    rows = sum(l.n for l in lins)
+    buf = torch.empty((rows, (k // 32) * 18), dtype=torch.uint8, device=gpu)
+    r, edges = 0, []
+    for lin in lins:
+        w = workload_weights_cached(wl, lin)
+        q4lib.q4_quantize(to_dev(w, gpu), packed=buf[r:r + lin.n])
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(buf[r:r + 8]), oracle.quantize(w[:8]))
+        assert np.array_equal(to_host(buf[r + lin.n - 8:r + lin.n]), oracle.quantize(w[-8:]))
+        del w
+        edges += [r, r + 1, r + lin.n - 2, r + lin.n - 1]
+        r += lin.n
+    packed = to_host(buf)
+    rng = np.random.default_rng(len(group))
+    cols = np.unique(np.concatenate([rng.choice(rows, size=1024, replace=False), edges]))
+    for m in (1, 10):
+        x = synth.workload_activations(wl, k, m)
+        y = to_host(q4lib.q4_gemv(to_dev(x, gpu), buf, y_dtype=torch.float16))
+        assert y.shape == (m, rows)
+        assert_matmul_close(y[:, cols], x, packed, rows, k, cols=cols,
+                            what=f"{'+'.join(group)} m{m}")
+
+
 def test_deterministic(q4lib, gpu):
     import torch
     n, k = 5120, 5120
