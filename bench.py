@@ -15,11 +15,16 @@ The same JSON line carries:
                    y) / mean launch time, against 8 TB/s HBM; `traffic` is the
                    HBM bytes per launch from the committed counter passes;
   gemm          -- prefill GEMM on the 2048 x 17408 x 5120 workload, whole
-                   batch and 8 chunks of 256 rows, TFLOP/s against fp16 MFMA;
+                   batch and 8 chunks of 256 rows, TFLOP/s against fp16 MFMA,
+                   plus the chunk-size sweep (128, 256 and 512 rows);
   quantize      -- the quantiser on the same 5120 x 5120 fp32 weight;
   layer_decode  -- one 27B-class layer's seven decode linears at M = 1 and 10,
                    as seven launches and as four (q/k/v and gate/up each one
                    launch on their concatenated packed rows);
+  layer_prefill -- the same layer's GEMMs at M = 256 and 4096, seven launches
+                   and four;
+  host_twin     -- the host-CPU twin (libq4host) on the same packed bytes,
+                   on the host cores (a second backend, not a GPU figure);
   cpu_baseline  -- the CPU oracle timed on a bounded sample of the step.
 
 Counter passes (HBM traffic): run `bench.py --traffic` once under
@@ -48,6 +53,7 @@ METRIC = "Q4_0 GEMV weight GB/s + GEMM TFLOPS, as % of MI355X HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 matrix peak
 BLOCK_BYTES, QK = 18, 32
+CHUNK_ROWS = (128, 256, 512)     # prefill chunk-size sweep over the 2048-row batch
 
 
 def kernel_source_hash() -> str:
@@ -157,7 +163,7 @@ def bench_gemv(q4, torch, dev, steps, warmup, rotate_bytes):
     return {
         "wl": s["wl"], "n": n, "k": k, "ms": ms, "wbytes": wbytes, "ncopies": s["ncopies"],
         "step_s": step_s, "value_gbs": wbytes * len(ms) / step_s / 1e9, "per_m": per_m,
-        "w_host": s["w_host"],
+        "w_host": s["w_host"], "packed0": s["packed"][0],
     }
 
 
@@ -193,36 +199,58 @@ def gemm_setup(q4, torch, dev):
     del w
     x = torch.from_numpy(synth.workload_activations(wl, k, m)).to(dev)
     y = torch.empty((m, n), dtype=torch.float16, device=dev)
-    ws = max(q4.q4_gemm_workspace_size(m, n, k), q4.q4_gemm_workspace_size(256, n, k), 1)
+    ws = max([q4.q4_gemm_workspace_size(c, n, k) for c in (m,) + CHUNK_ROWS] + [1])
     work = torch.empty(ws, dtype=torch.uint8, device=dev)
 
     def whole():
         q4.q4_gemm(x, packed, y=y, workspace=work)
 
-    def chunks():
-        for c in range(8):
-            q4.q4_gemm(x[c * 256:(c + 1) * 256], packed, y=y[c * 256:(c + 1) * 256], workspace=work)
+    def chunked(cs):
+        def fn():
+            for c in range(m // cs):
+                q4.q4_gemm(x[c * cs:(c + 1) * cs], packed, y=y[c * cs:(c + 1) * cs], workspace=work)
+        return fn
 
-    return m, n, k, whole, chunks
+    return m, n, k, whole, chunked
+
+
+def time_gemm_calls(torch, fn, reps):
+    """Mean GPU seconds of one fn() (its launches replayed from a HIP graph)."""
+    def rep():
+        for _ in range(reps):
+            fn()
+    g = capture(torch, rep)
+    g.replay()
+    t = replay_seconds(torch, g) / reps
+    del g
+    return t
 
 
 def bench_gemm(q4, torch, dev, reps):
-    m, n, k, whole, chunks = gemm_setup(q4, torch, dev)
+    """The 2048-row prefill of a 17408 x 5120 weight as one launch, as eight
+    256-row chunks (the serving page's chunk size), and the chunk-size sweep:
+    smaller chunks bound the activation memory a step holds, at the cost of
+    streaming the packed weight once per chunk and of fewer output tiles per
+    launch."""
+    m, n, k, whole, chunked = gemm_setup(q4, torch, dev)
+    flop = 2.0 * m * n * k
     res = {}
-    for name, fn, calls in (("whole_2048", whole, 1), ("chunked_8x256", chunks, 8)):
-        def rep():
-            for _ in range(reps):
-                fn()
-        g = capture(torch, rep)
-        g.replay()
-        avg_s = replay_seconds(torch, g) / reps
-        tf = 2.0 * m * n * k / avg_s / 1e12
+    for name, fn, calls in (("whole_2048", whole, 1), ("chunked_8x256", chunked(256), 8)):
+        avg_s = time_gemm_calls(torch, fn, reps)
+        tf = flop / avg_s / 1e12
         res[name] = {"mean_us": avg_s * 1e6, "launches": calls, "tflops": tf,
                      "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS}
+    sweep = []
+    for cs in CHUNK_ROWS:
+        avg_s = time_gemm_calls(torch, chunked(cs), reps)
+        tf = flop / avg_s / 1e12
+        sweep.append({"chunk_rows": cs, "launches": m // cs, "mean_us": avg_s * 1e6,
+                      "us_per_chunk": avg_s * 1e6 / (m // cs), "tflops": tf,
+                      "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS})
     best = res["whole_2048"]["tflops"]
     return {
         "workload": "prefill_chunked_2048x17408x5120", "m": m, "n": n, "k": k,
-        **res,
+        **res, "chunk_sweep": sweep,
         "roofline": {"bound": "mfma", "achieved": best, "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": best / MFMA_F16_PEAK_TFLOPS,
                      "traffic": load_traffic("gemm_2048x17408x5120")},
@@ -295,6 +323,95 @@ def bench_layer_decode(q4, torch, dev, steps, rotate_bytes, ms=(1, 10)):
         res[f"m{m}"] = row
     return {"workload": "decode_layer_27b_dense (q,k,v,o,gate,up,down)", "weight_bytes": layer_bytes,
             "layer_copies_rotated": copies, **res}
+
+
+def bench_layer_prefill(q4, torch, dev, reps, ms=(256, 4096)):
+    """Prefill through one 27B-class layer's seven linears at M = 256 (one
+    chunk) and 4096 rows: seven launches, and four with q/k/v and gate/up
+    each run on their concatenated packed rows.  The GEMM is bound by the
+    matrix cores, so one copy of the layer's weights serves every call."""
+    import synth
+    lins = {l.name: l for l in synth.WORKLOADS[5].linears}
+    groups = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gateup", ["gate", "up"]), ("down", ["down"])]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    bufs, views = {}, {}
+    for gname, names in groups:
+        kk = lins[names[0]].k
+        rows = sum(lins[nm].n for nm in names)
+        buf = torch.empty((rows, (kk // QK) * BLOCK_BYTES), dtype=torch.uint8, device=dev)
+        r = 0
+        for nm in names:
+            nn = lins[nm].n
+            views[nm] = buf[r:r + nn]
+            q4.q4_quantize(torch.randn((nn, kk), device=dev, generator=gen) * 0.02, packed=views[nm])
+            r += nn
+        bufs[gname] = buf
+    flop_per_row = 2.0 * sum(l.n * l.k for l in lins.values())
+    res = {}
+    for m in ms:
+        x = torch.randn((m, lins["q"].k), device=dev, generator=gen).half()
+        xd = torch.randn((m, lins["down"].k), device=dev, generator=gen).half()
+        ysep = {nm: torch.empty((m, l.n), dtype=torch.float16, device=dev) for nm, l in lins.items()}
+        ygrp = {g: torch.empty((m, sum(lins[nm].n for nm in names)), dtype=torch.float16, device=dev)
+                for g, names in groups}
+        wsz = max([q4.q4_gemm_workspace_size(m, b.shape[0], lins[names[0]].k)
+                   for (g, names), b in zip(groups, bufs.values())] +
+                  [q4.q4_gemm_workspace_size(m, l.n, l.k) for l in lins.values()] + [1])
+        work = torch.empty(wsz, dtype=torch.uint8, device=dev)
+
+        def separate():
+            for nm in ("q", "k", "v", "o", "gate", "up"):
+                q4.q4_gemm(x, views[nm], y=ysep[nm], workspace=work)
+            q4.q4_gemm(xd, views["down"], y=ysep["down"], workspace=work)
+
+        def fused():
+            for g in ("qkv", "o", "gateup"):
+                q4.q4_gemm(x, bufs[g], y=ygrp[g], workspace=work)
+            q4.q4_gemm(xd, bufs["down"], y=ygrp["down"], workspace=work)
+
+        row = {}
+        for name, fn, launches in (("separate", separate, 7), ("fused", fused, 4)):
+            t = time_gemm_calls(torch, fn, reps)
+            tf = flop_per_row * m / t / 1e12
+            row[name] = {"launches": launches, "us_per_layer": t * 1e6, "tflops": tf,
+                         "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS}
+        res[f"m{m}"] = row
+        del x, xd, ysep, ygrp, work
+    return {"workload": "prefill_layer_27b_dense (q,k,v,o,gate,up,down)",
+            "gflop_per_row": flop_per_row / 1e9, **res}
+
+
+def bench_host_twin(q4, torch, packed_dev, n, k, ms, budget_s=1.0):
+    """The host-CPU twin (libq4host) on the same packed bytes as the headline
+    GEMV, copied once to host memory: each batch size repeated for about
+    budget_s seconds on the default thread count.  A second backend's rate on
+    the host cores, not a GPU figure."""
+    import numpy as np
+    import synth
+    from bit_block_quantized_q4_amd.host import q4_host_default_threads, q4_host_gemv
+    packed = packed_dev.cpu().numpy()
+    wl = synth.WORKLOADS[2]
+    xs = synth.workload_activations(wl, k, max(ms))
+    wbytes = packed.nbytes
+    threads = q4_host_default_threads()
+    per_m, step = [], 0.0
+    for m in ms:
+        x = np.ascontiguousarray(xs[:m])
+        y = np.empty((m, n), np.float16)
+        q4_host_gemv(x, packed, y=y)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            q4_host_gemv(x, packed, y=y)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+        avg = el / reps
+        step += avg
+        per_m.append({"m": m, "mean_ms": avg * 1e3, "weight_gbs": wbytes / avg / 1e9})
+    return {"workload": f"decode_attn_proj_{n}x{k} (host memory)", "threads": threads,
+            "value": wbytes * len(ms) / step / 1e9, "unit": "GB/s", "per_m": per_m}
 
 
 # ------------------------------------------------------------ HBM traffic
@@ -465,7 +582,8 @@ def main():
     ap.add_argument("--rotate-mib", type=int, default=1024)
     ap.add_argument("--gemm-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "gemv", "gemm", "quantize", "layer"], default="all")
+    ap.add_argument("--only", choices=["all", "gemv", "gemm", "quantize", "layer", "host"],
+                    default="all")
     ap.add_argument("--traffic", action="store_true",
                     help="run the launches the FETCH_SIZE / WRITE_SIZE counter passes read")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -525,6 +643,9 @@ def main():
         out["gemm"] = bench_gemm(q4, torch, dev, args.gemm_reps)
     if args.only in ("all", "layer"):
         out["layer_decode"] = bench_layer_decode(q4, torch, dev, min(args.steps, 50), rotate)
+        out["layer_prefill"] = bench_layer_prefill(q4, torch, dev, 3)
+    if args.only in ("all", "host"):
+        out["host_twin"] = bench_host_twin(q4, torch, g["packed0"], g["n"], g["k"], g["ms"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(g["w_host"], g["n"], g["k"], g["ms"])
     out["kernel_source_hash"] = kernel_source_hash()

@@ -1,4 +1,4 @@
-"""Build libq4.so for gfx950 in-tree.
+"""Build libq4.so for gfx950 (and the host-CPU twin libq4host.so) in-tree.
 
 Usage: ``python -m bit_block_quantized_q4_amd.build`` (or ``build()``).
 Every HIP translation unit is compiled with hipcc for ``--offload-arch=gfx950``
@@ -20,6 +20,8 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 BUILD_DIR = PKG / "_build"
 LIB_PATH = PKG / "libq4.so"
+HOST_SRC = PKG / "host" / "q4_host.cpp"
+HOST_LIB_PATH = PKG / "libq4host.so"
 ARCH = os.environ.get("Q4_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [
@@ -69,8 +71,21 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
+def build_host(verbose: bool = False) -> Path:
+    """Compile the host-CPU twin (host/q4_host.cpp, plain C++ with AVX2 code
+    behind run-time checks) into libq4host.so; returns its path."""
+    cxx = os.environ.get("CXX", "g++")
+    tmp = HOST_LIB_PATH.with_suffix(".so.tmp")
+    _run([cxx, "-O3", "-std=c++17", "-fPIC", "-shared", "-pthread", "-Wall",
+          "-ffp-contract=off", f"-I{INCLUDE}", str(HOST_SRC), "-o", str(tmp)], verbose)
+    os.replace(tmp, HOST_LIB_PATH)
+    return HOST_LIB_PATH
+
+
 def build(verbose: bool = False) -> Path:
-    """Compile every csrc/*.hip for gfx950 and link libq4.so; returns its path."""
+    """Compile every csrc/*.hip for gfx950 and link libq4.so (and build the
+    host-CPU twin libq4host.so); returns libq4.so's path."""
+    build_host(verbose)
     hipcc = _hipcc()
     BUILD_DIR.mkdir(exist_ok=True)
     srcs = sorted(CSRC.glob("*.hip"))

@@ -59,6 +59,7 @@ const char* q4_status_string(int status) {
     case Q4_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
     case Q4_ERR_HIP: return "HIP runtime refused the kernel launch";
     case Q4_ERR_WORKSPACE: return "workspace missing or too small";
+    case Q4_ERR_UNSUPPORTED: return "the host CPU lacks AVX2, FMA or F16C";
     default: return "unknown q4 status";
   }
 }

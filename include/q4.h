@@ -76,7 +76,9 @@ typedef enum q4_status {
   Q4_ERR_DTYPE = 3,       /* dtype code not supported by this call */
   Q4_ERR_ALIGNMENT = 4,   /* a pointer is not 16-byte aligned */
   Q4_ERR_HIP = 5,         /* the HIP runtime refused a launch */
-  Q4_ERR_WORKSPACE = 6    /* workspace missing or smaller than required */
+  Q4_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
+  Q4_ERR_UNSUPPORTED = 7  /* the host CPU lacks an instruction set the call needs
+                             (q4_host.h) */
 } q4_status;
 
 typedef enum q4_dtype {

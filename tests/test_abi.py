@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(q4lib):
 
 def test_version_and_status_strings(q4lib):
     assert q4lib.q4_abi_version() == 1
-    for code in range(7):
+    for code in range(8):
         s = q4lib.q4_status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in q4lib.q4_status_string(99)
