@@ -23,6 +23,7 @@ The same JSON line carries:
                    launch on their concatenated packed rows);
   layer_prefill -- the same layer's GEMMs at M = 256 and 4096, seven launches
                    and four;
+  bf16          -- bf16 activations on the headline GEMV and the prefill GEMM;
   host_twin     -- the host-CPU twin (libq4host) on the same packed bytes,
                    on the host cores (a second backend, not a GPU figure);
   cpu_baseline  -- the CPU oracle timed on a bounded sample of the step.
@@ -163,7 +164,7 @@ def bench_gemv(q4, torch, dev, steps, warmup, rotate_bytes):
     return {
         "wl": s["wl"], "n": n, "k": k, "ms": ms, "wbytes": wbytes, "ncopies": s["ncopies"],
         "step_s": step_s, "value_gbs": wbytes * len(ms) / step_s / 1e9, "per_m": per_m,
-        "w_host": s["w_host"], "packed0": s["packed"][0],
+        "w_host": s["w_host"], "packed0": s["packed"][0], "setup": s,
     }
 
 
@@ -189,7 +190,7 @@ def bench_quantize(q4, torch, dev, w_host, reps, rotate_bytes):
                          "traffic": load_traffic("quantize_fp32_5120x5120")}}
 
 
-def gemm_setup(q4, torch, dev):
+def gemm_setup(q4, torch, dev, x_dtype=None):
     import synth
     wl = synth.WORKLOADS[4]
     lin = wl.linears[0]
@@ -198,8 +199,11 @@ def gemm_setup(q4, torch, dev):
     packed = q4.q4_quantize(torch.from_numpy(w).to(dev))
     del w
     x = torch.from_numpy(synth.workload_activations(wl, k, m)).to(dev)
+    if x_dtype is not None:
+        x = x.to(x_dtype)
     y = torch.empty((m, n), dtype=torch.float16, device=dev)
-    ws = max([q4.q4_gemm_workspace_size(c, n, k) for c in (m,) + CHUNK_ROWS] + [1])
+    xcode = q4._dtype_code(x)
+    ws = max([q4.q4_gemm_workspace_size_dt(c, n, k, xcode) for c in (m,) + CHUNK_ROWS] + [1])
     work = torch.empty(ws, dtype=torch.uint8, device=dev)
 
     def whole():
@@ -414,6 +418,34 @@ def bench_host_twin(q4, torch, packed_dev, n, k, ms, budget_s=1.0):
             "value": wbytes * len(ms) / step / 1e9, "unit": "GB/s", "per_m": per_m}
 
 
+def bench_bf16(q4, torch, dev, s, steps, gemm_reps):
+    """bf16 activations: the headline GEMV on the same rotated weights (the
+    kernels convert x to fp16 in LDS or in registers), and the 2048-row
+    prefill, whole and in 256-row chunks (x staged as fp16 in the workspace
+    by a pre-pass, which is inside the timed launches)."""
+    n, k, wbytes = s["n"], s["k"], s["wbytes"]
+    sb = dict(s, x=s["x"].to(torch.bfloat16))
+    per_m = []
+    for m in s["ms"]:
+        g = capture(torch, gemv_launches(q4, sb, steps, [m], 0))
+        g.replay()
+        avg_s = replay_seconds(torch, g) / steps
+        del g
+        alg = gemv_alg_bytes(m, n, k)
+        per_m.append({"m": m, "mean_us": avg_s * 1e6, "alg_gbs": alg / avg_s / 1e9,
+                      "frac_hbm": alg / avg_s / 1e9 / HBM_PEAK_GBS})
+    m, n2, k2, whole, chunked = gemm_setup(q4, torch, dev, torch.bfloat16)
+    flop = 2.0 * m * n2 * k2
+    gemm = {}
+    for name, fn, calls in (("whole_2048", whole, 1), ("chunked_8x256", chunked(256), 8)):
+        t = time_gemm_calls(torch, fn, gemm_reps)
+        tf = flop / t / 1e12
+        gemm[name] = {"mean_us": t * 1e6, "launches": calls, "tflops": tf,
+                      "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS}
+    return {"gemv_workload": f"decode_attn_proj_{n}x{k}, bf16 x, fp16 y", "gemv_per_m": per_m,
+            "gemm_workload": f"prefill_{m}x{n2}x{k2}, bf16 x, fp16 y", "gemm": gemm}
+
+
 # ------------------------------------------------------------ HBM traffic
 
 TRAFFIC_CALIB_BYTES = 512 << 20
@@ -582,7 +614,7 @@ def main():
     ap.add_argument("--rotate-mib", type=int, default=1024)
     ap.add_argument("--gemm-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "gemv", "gemm", "quantize", "layer", "host"],
+    ap.add_argument("--only", choices=["all", "gemv", "gemm", "quantize", "layer", "host", "bf16"],
                     default="all")
     ap.add_argument("--traffic", action="store_true",
                     help="run the launches the FETCH_SIZE / WRITE_SIZE counter passes read")
@@ -644,6 +676,8 @@ def main():
     if args.only in ("all", "layer"):
         out["layer_decode"] = bench_layer_decode(q4, torch, dev, min(args.steps, 50), rotate)
         out["layer_prefill"] = bench_layer_prefill(q4, torch, dev, 3)
+    if args.only in ("all", "bf16"):
+        out["bf16"] = bench_bf16(q4, torch, dev, g["setup"], args.steps, args.gemm_reps)
     if args.only in ("all", "host"):
         out["host_twin"] = bench_host_twin(q4, torch, g["packed0"], g["n"], g["k"], g["ms"])
     if not args.no_cpu_baseline:

@@ -8,7 +8,7 @@ library has not been built, every call raises ``Q4LibraryMissing`` (build it
 with ``python -m bit_block_quantized_q4_amd.build``).
 
 Functions mirror the C entry points: ``q4_packed_size``,
-``q4_gemm_workspace_size``, ``q4_quantize``, ``q4_gemv``, ``q4_gemm``,
+``q4_gemm_workspace_size``, ``q4_gemm_workspace_size_dt``, ``q4_quantize``, ``q4_gemv``, ``q4_gemm``,
 ``q4_status_string``, ``q4_abi_version``.
 """
 
@@ -37,6 +37,7 @@ Q4_ERR_WORKSPACE = 6
 
 Q4_F32 = 0
 Q4_F16 = 1
+Q4_BF16 = 2
 
 # Every function the header declares, with (restype, argtypes).
 _SIGS = {
@@ -44,6 +45,7 @@ _SIGS = {
     "q4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "q4_packed_size": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
     "q4_gemm_workspace_size": (ctypes.c_size_t, [ctypes.c_int64] * 3),
+    "q4_gemm_workspace_size_dt": (ctypes.c_size_t, [ctypes.c_int64] * 3 + [ctypes.c_int]),
     "q4_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     "q4_gemv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
@@ -132,6 +134,10 @@ def q4_gemm_workspace_size(m: int, n: int, k: int) -> int:
     return lib().q4_gemm_workspace_size(int(m), int(n), int(k))
 
 
+def q4_gemm_workspace_size_dt(m: int, n: int, k: int, x_dtype: int) -> int:
+    return lib().q4_gemm_workspace_size_dt(int(m), int(n), int(k), int(x_dtype))
+
+
 # ------------------------------------------------------------ torch marshalling
 
 def _torch():
@@ -145,7 +151,9 @@ def _dtype_code(t) -> int:
         return Q4_F32
     if t.dtype == torch.float16:
         return Q4_F16
-    raise TypeError(f"unsupported dtype {t.dtype}; libq4 takes float32 or float16")
+    if t.dtype == torch.bfloat16:
+        return Q4_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; libq4 takes float32, float16 or bfloat16")
 
 
 def _torch_dtype(code_or_dtype):
@@ -205,7 +213,9 @@ def q4_quantize(w, packed=None, stream=None):
 def _out(x, m, n, y, y_dtype):
     torch = _torch()
     if y is None:
-        y = torch.empty((m, n), dtype=_torch_dtype(y_dtype if y_dtype is not None else x.dtype),
+        # outputs are fp32 or fp16: bf16 activations default to an fp32 output
+        dflt = torch.float32 if x.dtype == torch.bfloat16 else x.dtype
+        y = torch.empty((m, n), dtype=_torch_dtype(y_dtype if y_dtype is not None else dflt),
                         device=x.device)
     _need_device(y, "y")
     return y
@@ -231,7 +241,7 @@ def q4_gemm(x, packed, y=None, y_dtype=None, workspace=None, stream=None, n=None
     n, k = packed_shape(packed, n, k)
     m = int(x.numel() // k) if x.dim() != 2 else int(x.shape[0])
     y = _out(x, m, n, y, y_dtype)
-    need = q4_gemm_workspace_size(m, n, k)
+    need = q4_gemm_workspace_size_dt(m, n, k, _dtype_code(x))
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wptr = workspace.data_ptr() if workspace is not None else None

@@ -11,7 +11,9 @@ constexpr int64_t kMaxRows = int64_t(1) << 31;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool valid_dtype(int dt) { return dt == Q4_F32 || dt == Q4_F16; }
+// Inputs (weights, activations) may be bf16; outputs are fp32 or fp16.
+bool valid_in_dtype(int dt) { return dt == Q4_F32 || dt == Q4_F16 || dt == Q4_BF16; }
+bool valid_out_dtype(int dt) { return dt == Q4_F32 || dt == Q4_F16; }
 
 size_t dtype_bytes(int dt) { return dt == Q4_F32 ? 4 : 2; }
 
@@ -35,7 +37,7 @@ q4_status check_matmul(const void* x, int x_dtype, const void* packed, void* y,
   if (!valid_nk(n, k) || m < 1 || m >= kMaxRows || m > kMaxElems / k ||
       m > kMaxElems / n)
     return Q4_ERR_SHAPE;
-  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return Q4_ERR_DTYPE;
+  if (!valid_in_dtype(x_dtype) || !valid_out_dtype(y_dtype)) return Q4_ERR_DTYPE;
   if (!aligned16(x) || !aligned16(packed) || !aligned16(y)) return Q4_ERR_ALIGNMENT;
   const size_t ybytes = static_cast<size_t>(m) * n * dtype_bytes(y_dtype);
   const size_t xbytes = static_cast<size_t>(m) * k * dtype_bytes(x_dtype);
@@ -73,7 +75,7 @@ q4_status q4_quantize(const void* w, int w_dtype, int64_t n, int64_t k, void* pa
                       q4_stream_t stream) {
   if (!w || !packed) return Q4_ERR_INVALID_ARG;
   if (!valid_nk(n, k)) return Q4_ERR_SHAPE;
-  if (!valid_dtype(w_dtype)) return Q4_ERR_DTYPE;
+  if (!valid_in_dtype(w_dtype)) return Q4_ERR_DTYPE;
   if (!aligned16(w) || !aligned16(packed)) return Q4_ERR_ALIGNMENT;
   if (overlap(w, static_cast<size_t>(n) * k * dtype_bytes(w_dtype), packed,
               q4_packed_size(n, k)))
@@ -95,8 +97,13 @@ q4_status q4_gemv(const void* x, int x_dtype, const void* packed, void* y, int y
 }
 
 size_t q4_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
-  if (!valid_nk(n, k) || m < 1 || m >= kMaxRows) return 0;
-  return q4::gemm_workspace_bytes(m, n, k);
+  return q4_gemm_workspace_size_dt(m, n, k, Q4_F16);
+}
+
+size_t q4_gemm_workspace_size_dt(int64_t m, int64_t n, int64_t k, int x_dtype) {
+  if (!valid_nk(n, k) || m < 1 || m >= kMaxRows || m > kMaxElems / k) return 0;
+  if (x_dtype != Q4_F16 && x_dtype != Q4_BF16) return 0;
+  return q4::gemm_workspace_bytes(m, n, k, static_cast<q4::DType>(x_dtype));
 }
 
 q4_status q4_gemm(const void* x, int x_dtype, const void* packed, void* y, int y_dtype,
@@ -104,13 +111,19 @@ q4_status q4_gemm(const void* x, int x_dtype, const void* packed, void* y, int y
                   size_t workspace_bytes, q4_stream_t stream) {
   const q4_status st = check_matmul(x, x_dtype, packed, y, y_dtype, m, n, k);
   if (st != Q4_OK) return st;
-  if (x_dtype != Q4_F16) return Q4_ERR_DTYPE;
-  const size_t need = q4::gemm_workspace_bytes(m, n, k);
+  if (x_dtype != Q4_F16 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+  const size_t need = q4::gemm_workspace_bytes(m, n, k, static_cast<q4::DType>(x_dtype));
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
     if (!aligned16(workspace)) return Q4_ERR_ALIGNMENT;
+    const size_t xbytes = static_cast<size_t>(m) * k * 2;
+    if (overlap(workspace, need, x, xbytes) || overlap(workspace, need, y,
+                static_cast<size_t>(m) * n * dtype_bytes(y_dtype)) ||
+        overlap(workspace, need, packed, q4_packed_size(n, k)))
+      return Q4_ERR_INVALID_ARG;
   }
-  return from_hip(q4::launch_gemm(x, q4::DType::F16, static_cast<const uint8_t*>(packed),
+  return from_hip(q4::launch_gemm(x, static_cast<q4::DType>(x_dtype),
+                                  static_cast<const uint8_t*>(packed),
                                   y, static_cast<q4::DType>(y_dtype), m, n, k,
                                   need > 0 ? workspace : nullptr,
                                   reinterpret_cast<hipStream_t>(stream)));

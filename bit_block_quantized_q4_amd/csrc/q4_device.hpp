@@ -102,6 +102,14 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   asm volatile("" ::: "memory");
 }
 
+// Wait until every LDS operation of this wave has completed (vector-memory
+// copies may stay in flight).
+__device__ __forceinline__ void wait_lgkm0() {
+  // vmcnt at its maximum (63), expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+  asm volatile("" ::: "memory");
+}
+
 // As wait_vm / wait_vm_lgkm0 for a run-time count n <= MAXN (a chain of
 // uniform compares choosing the immediate).
 template <int MAXN>

@@ -874,12 +874,55 @@ hipError_t dispatch_tiled(const half_t* x, const uint8_t* packed, YT* y, int64_t
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) { return gemm_plan(m, n, k).ws_bytes; }
+namespace {
 
-hipError_t launch_gemm(const void* x, DType, const uint8_t* packed, void* y,
+// Converted bf16 activations occupy the workspace's first bytes.
+int64_t bf16_stage_bytes(int64_t m, int64_t k) { return (m * k * 2 + 255) / 256 * 256; }
+
+// bf16 activations -> fp16 (round to nearest even; exact for every value fp16
+// represents), eight values per thread per step.  ndw (dwords) is a multiple
+// of 4 (k is a multiple of 32), and both buffers are 16-byte aligned.
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint32_t* __restrict__ x,
+                                                          uint32_t* __restrict__ out, int64_t ndw) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const int64_t nq = ndw / 4;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < nq; i += stride) {
+    u32x4_t v = reinterpret_cast<const u32x4_t*>(x)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+    reinterpret_cast<u32x4_t*>(out)[i] = v;
+  }
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, DType xt) {
+  const size_t tiles = gemm_plan(m, n, k).ws_bytes;
+  return xt == DType::BF16 ? static_cast<size_t>(bf16_stage_bytes(m, k)) + tiles : tiles;
+}
+
+hipError_t launch_gemm(const void* x, DType xt, const uint8_t* packed, void* y,
                        DType yt, int64_t m, int64_t n, int64_t k, void* workspace,
                        hipStream_t s) {
   const half_t* xp = static_cast<const half_t*>(x);
+  if (xt == DType::BF16) {
+    // Stage the activations as fp16 in the workspace, then run the fp16 path
+    // on them with the rest of the workspace.
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const int64_t ndw = m * k / 2;
+    const int64_t blocks = (ndw / 4 + 255) / 256;
+    const dim3 grid(static_cast<unsigned>(blocks < 4096 ? blocks : 4096));
+    const uint32_t* src = static_cast<const uint32_t*>(x);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(ws);
+    int64_t nd = ndw;
+    void* argv[] = {&src, &dst, &nd};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bf16_to_f16_kernel), grid,
+                                         dim3(256), argv, 0, s);
+    if (e != hipSuccess) return e;
+    xp = reinterpret_cast<const half_t*>(ws);
+    workspace = gemm_plan(m, n, k).ws_bytes > 0 ? ws + bf16_stage_bytes(m, k) : nullptr;
+  }
   if (k % kBK == 0) {
     if (yt == DType::F16)
       return dispatch_tiled(xp, packed, static_cast<half_t*>(y), m, n, k, workspace, s);

@@ -30,8 +30,14 @@
 // product with four fp32 FMAs.  The waves' partial tiles are summed in LDS in
 // wave order at the end.
 //
-// Generic kernel (fp32 activations or k % 256 != 0): one wavefront per output
-// feature, lanes stride over blocks, wave-wide xor-shuffle reduction.
+// Generic kernel (fp32 activations, or bf16 activations with k % 512 != 0,
+// or k % 256 != 0): one wavefront per output feature, lanes stride over
+// blocks, wave-wide xor-shuffle reduction.
+//
+// bf16 activations: the balanced and tile kernels convert them to fp16 in
+// the kernel (round to nearest even; exact for every value fp16 represents)
+// and then run their fp16 matrix-core path; the generic kernel widens them
+// exactly to fp32.
 #include "q4_device.hpp"
 
 namespace q4 {
@@ -39,6 +45,7 @@ namespace {
 
 template <typename T>
 __device__ __forceinline__ float to_f32(T v) { return static_cast<float>(v); }
+__device__ __forceinline__ float to_f32(bf16_t v) { return bf16_bits_to_float(v.bits); }
 
 template <typename T>
 __device__ __forceinline__ T from_f32(float v) { return static_cast<T>(v); }
@@ -394,7 +401,9 @@ __host__ __device__ inline BalLds bal_lds(int m, int64_t k, int rg, int nw, int 
   return L;
 }
 
-template <int NW, int P, int MR>
+// XB: the activations arrive as bf16 and are converted to fp16 in LDS, in
+// place, once staged (exact for every value fp16 represents).
+template <int NW, int P, int MR, bool XB>
 __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, void* __restrict__ y,
     int m, int64_t n, int64_t k, int rows_per_wg, int y_f16) {
@@ -540,6 +549,39 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
     accr = float4_t{0.f, 0.f, 0.f, 0.f};
   };
 
+  // bf16 activations: every wave's x copies have landed (the barrier before
+  // this); convert the staged rows to fp16 in place, then a second barrier
+  // (task copies stay in flight through it).
+  auto convert_x = [&]() {
+    if constexpr (XB) {
+      // 16-byte pieces (eight values), four per thread in flight
+      u32x4* xq = reinterpret_cast<u32x4*>(xs);
+      const int64_t nq = static_cast<int64_t>(m) * k / 8;
+      constexpr int kT = NW * kWave;
+      int64_t i = threadIdx.x;
+      for (; i + 3 * kT < nq; i += 4 * kT) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = xq[i + u * kT];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[u][e] = bf16x2_to_f16x2(v[u][e]);
+          xq[i + u * kT] = v[u];
+        }
+      }
+      for (; i < nq; i += kT) {
+        u32x4 v = xq[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+        xq[i] = v;
+      }
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+    }
+  };
+
   static_assert((P & (P - 1)) == 0, "ring size must be a power of two");
   if (t0 < t1) {
     const int ntask = t1 - t0;
@@ -560,6 +602,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
     wait_vm_lgkm0_upto<2 * P>(2 * npro);
     __builtin_amdgcn_s_barrier();
     compiler_fence();
+    convert_x();
     int cset = t0 - (t0 / S) * S, crg = t0 / S;
     auto finish = [&](int t) {
       compute(ring + (t & (P - 1)) * kTaskBytes, cset);
@@ -590,6 +633,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
   } else {
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();  // matches the barrier of the waves with tasks
+    convert_x();
   }
 
   __syncthreads();
@@ -638,10 +682,10 @@ bool bal_plan(int m, int64_t n, int64_t k, BalPlan* p) {
   return false;
 }
 
-template <int NW, int MR>
+template <int NW, int MR, bool XB>
 hipError_t launch_bal_t(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
                         int64_t n, int64_t k, const BalPlan& p, hipStream_t s) {
-  const void* fn = reinterpret_cast<const void*>(&gemv_bal_kernel<NW, kBalP, MR>);
+  const void* fn = reinterpret_cast<const void*>(&gemv_bal_kernel<NW, kBalP, MR, XB>);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -656,19 +700,20 @@ hipError_t launch_bal_t(const void* x, const uint8_t* packed, void* y, bool y_f1
                          static_cast<size_t>(p.lds), s);
 }
 
-template <int MR>
+template <int MR, bool XB>
 hipError_t dispatch_bal_m(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
                           int64_t n, int64_t k, const BalPlan& p, hipStream_t s) {
-  if (p.nw == 16) return launch_bal_t<16, MR>(x, packed, y, y_f16, m, n, k, p, s);
-  return launch_bal_t<8, MR>(x, packed, y, y_f16, m, n, k, p, s);
+  if (p.nw == 16) return launch_bal_t<16, MR, XB>(x, packed, y, y_f16, m, n, k, p, s);
+  return launch_bal_t<8, MR, XB>(x, packed, y, y_f16, m, n, k, p, s);
 }
 
 // MR: activation rows accumulated (m rounded up to 1, 2 or 4).
+template <bool XB>
 hipError_t dispatch_bal(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
                         int64_t n, int64_t k, const BalPlan& p, hipStream_t s) {
-  if (m == 1) return dispatch_bal_m<1>(x, packed, y, y_f16, m, n, k, p, s);
-  if (m == 2) return dispatch_bal_m<2>(x, packed, y, y_f16, m, n, k, p, s);
-  return dispatch_bal_m<4>(x, packed, y, y_f16, m, n, k, p, s);
+  if (m == 1) return dispatch_bal_m<1, XB>(x, packed, y, y_f16, m, n, k, p, s);
+  if (m == 2) return dispatch_bal_m<2, XB>(x, packed, y, y_f16, m, n, k, p, s);
+  return dispatch_bal_m<4, XB>(x, packed, y, y_f16, m, n, k, p, s);
 }
 
 }  // namespace
@@ -689,15 +734,22 @@ int device_cu_count() {
 hipError_t launch_gemv(const void* x, DType xt, const uint8_t* packed, void* y,
                        DType yt, int m, int64_t n, int64_t k, hipStream_t s) {
   BalPlan plan;
-  if (xt == DType::F16 && bal_plan(m, n, k, &plan))
-    return dispatch_bal(x, packed, y, yt == DType::F16, m, n, k, plan, s);
-  if (xt == DType::F16 && gemv_tile_supports(m, k))
-    return launch_gemv_tile(x, packed, y, yt == DType::F16, m, n, k, s);
-  if (xt == DType::F16 && stream_supports(k))
+  const bool xh = xt == DType::F16, xb = xt == DType::BF16;
+  if (xh && bal_plan(m, n, k, &plan))
+    return dispatch_bal<false>(x, packed, y, yt == DType::F16, m, n, k, plan, s);
+  if (xb && bal_plan(m, n, k, &plan))
+    return dispatch_bal<true>(x, packed, y, yt == DType::F16, m, n, k, plan, s);
+  if ((xh || xb) && gemv_tile_supports(m, k))
+    return launch_gemv_tile(x, xb, packed, y, yt == DType::F16, m, n, k, s);
+  if (xh && stream_supports(k))
     return dispatch_stream(x, packed, y, yt == DType::F16, m, n, k, s);
-  if (xt == DType::F16) {
+  if (xh) {
     if (yt == DType::F16) return dispatch_rowwave<half_t, half_t>(x, packed, y, m, n, k, s);
     return dispatch_rowwave<half_t, float>(x, packed, y, m, n, k, s);
+  }
+  if (xb) {
+    if (yt == DType::F16) return dispatch_rowwave<bf16_t, half_t>(x, packed, y, m, n, k, s);
+    return dispatch_rowwave<bf16_t, float>(x, packed, y, m, n, k, s);
   }
   if (yt == DType::F16) return dispatch_rowwave<float, half_t>(x, packed, y, m, n, k, s);
   return dispatch_rowwave<float, float>(x, packed, y, m, n, k, s);

@@ -11,7 +11,7 @@ constexpr int kQK = 32;          // weights per block
 constexpr int kBlockBytes = 18;  // fp16 scale + 16 code bytes
 constexpr int kWave = 64;        // CDNA wavefront
 
-enum class DType : int { F32 = 0, F16 = 1 };
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
 
 typedef _Float16 half_t;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -25,6 +25,26 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t bits) {
   return static_cast<float>(__builtin_bit_cast(half_t, bits));
 }
 
+// bfloat16 storage: the upper half of an IEEE binary32 pattern.
+struct bf16_t {
+  uint16_t bits;
+};
+
+// bf16 bit pattern -> fp32 (exact: the pattern shifted into the upper half).
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits) {
+  return __builtin_bit_cast(float, bits << 16);
+}
+
+// Two bf16 values packed in a dword (element 0 in the low half) -> the same
+// two values as fp16, rounded to nearest even: exact for every value fp16
+// represents (all bf16 values with 2^-14 <= |v| <= 65504 among them).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
+  const float lo = __builtin_bit_cast(float, v << 16);
+  const float hi = __builtin_bit_cast(float, v & 0xFFFF0000u);
+  const half2_t h = {static_cast<half_t>(lo), static_cast<half_t>(hi)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // Launchers (return the launch status; never synchronise).
 hipError_t launch_quantize(const void* w, DType wt, int64_t n, int64_t k,
                            uint8_t* packed, hipStream_t s);
@@ -35,12 +55,14 @@ hipError_t launch_gemv(const void* x, DType xt, const uint8_t* packed, void* y,
 // Compute units of the current device (cached per device; 256 if unknown).
 int device_cu_count();
 
-// Decode GEMV on 16x16x32 matrix cores (k a multiple of 1024, m <= 32).
+// Decode GEMV on 16x16x32 matrix cores (k a multiple of 512, m <= 32).
 bool gemv_tile_supports(int m, int64_t k);
-hipError_t launch_gemv_tile(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
-                            int64_t n, int64_t k, hipStream_t s);
+hipError_t launch_gemv_tile(const void* x, bool x_bf16, const uint8_t* packed, void* y,
+                            bool y_f16, int m, int64_t n, int64_t k, hipStream_t s);
 
-size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+// Workspace of a GEMM whose activations have dtype xt: bf16 activations are
+// first converted to fp16 into its leading m * k * 2 bytes (rounded up to 256).
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, DType xt);
 hipError_t launch_gemm(const void* x, DType xt, const uint8_t* packed, void* y,
                        DType yt, int64_t m, int64_t n, int64_t k,
                        void* workspace, hipStream_t s);

@@ -13,7 +13,8 @@
 // maximum is a 3-step DPP reduction inside each group of eight; the
 // high-nibble codes of elements 16..31 (lanes 4..7) are moved down onto
 // lanes 0..3, which then own four finished code bytes each.  The kernel
-// reads 4 (fp32) or 2 (fp16) bytes and writes 0.5625 bytes per weight.  The
+// reads 4 (fp32) or 2 (fp16, bf16; both widened exactly to fp32) bytes and
+// writes 0.5625 bytes per weight.  The
 // codes follow the correctly rounded fp32 division exactly: a reciprocal with
 // one residual step decides every code whose t is not within 2^-16 of an
 // integer, the rest redo the IEEE division (the library is built without
@@ -34,6 +35,16 @@ struct Load4<float> {
   static __device__ __forceinline__ void run(const float* p, float v[4]) {
     const float4 t = *reinterpret_cast<const float4*>(p);
     v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  }
+};
+
+template <>
+struct Load4<bf16_t> {
+  static __device__ __forceinline__ void run(const bf16_t* p, float v[4]) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t t = *reinterpret_cast<const u32x2_t*>(p);
+    v[0] = bf16_bits_to_float(t[0] & 0xFFFFu); v[1] = bf16_bits_to_float(t[0] >> 16);
+    v[2] = bf16_bits_to_float(t[1] & 0xFFFFu); v[3] = bf16_bits_to_float(t[1] >> 16);
   }
 };
 
@@ -181,6 +192,12 @@ hipError_t launch_quantize(const void* w, DType wt, int64_t n, int64_t k,
     const float* p = static_cast<const float*>(w);
     void* argv[] = {&p, &packed, const_cast<int64_t*>(&nblocks)};
     return hipLaunchKernel(reinterpret_cast<const void*>(&quantize_kernel<float, kQuantUF32>),
+                           grid, block, argv, 0, s);
+  }
+  if (wt == DType::BF16) {
+    const bf16_t* p = static_cast<const bf16_t*>(w);
+    void* argv[] = {&p, &packed, const_cast<int64_t*>(&nblocks)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&quantize_kernel<bf16_t, kQuantUF16>),
                            grid, block, argv, 0, s);
   }
   const half_t* p = static_cast<const half_t*>(w);

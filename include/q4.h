@@ -83,7 +83,9 @@ typedef enum q4_status {
 
 typedef enum q4_dtype {
   Q4_F32 = 0, /* IEEE binary32 */
-  Q4_F16 = 1  /* IEEE binary16 */
+  Q4_F16 = 1, /* IEEE binary16 */
+  Q4_BF16 = 2 /* bfloat16: the upper 16 bits of a binary32 pattern; accepted
+                 for weights and activations, not for outputs */
 } q4_dtype;
 
 /* Version of this ABI (Q4_ABI_VERSION). */
@@ -96,28 +98,39 @@ const char *q4_status_string(int status);
  * Returns 0 when the shape is invalid (n < 1, k < 32, k % 32 != 0). */
 size_t q4_packed_size(int64_t n, int64_t k);
 
-/* Quantise a row-major [n][k] weight `w` of dtype `w_dtype` (Q4_F32 or
- * Q4_F16; fp16 is widened exactly to fp32 first) into `packed`, which must
- * hold q4_packed_size(n, k) bytes.  The result is bit-identical to the rule
- * stated at the top of this header.  Reads 4 (fp32) or 2 (fp16) bytes and
- * writes 0.5625 bytes per weight. */
+/* Quantise a row-major [n][k] weight `w` of dtype `w_dtype` (Q4_F32, Q4_F16
+ * or Q4_BF16; fp16 and bf16 are widened exactly to fp32 first) into `packed`,
+ * which must hold q4_packed_size(n, k) bytes.  The result is bit-identical to
+ * the rule stated at the top of this header.  Reads 4 (fp32) or 2 (fp16,
+ * bf16) bytes and writes 0.5625 bytes per weight. */
 q4_status q4_quantize(const void *w, int w_dtype, int64_t n, int64_t k,
                       void *packed, q4_stream_t stream);
 
 /* Batched-decode GEMV: y[m][n] = x[m][k] . dequant(packed)^T for
- * 1 <= m <= Q4_GEMV_MAX_M (the page's batched decode stage).  x is Q4_F32 or
- * Q4_F16, y is Q4_F32 or Q4_F16.  Every output is the fp32 sum over blocks of
- * d times the block dot product of x with (q - 8), rounded once to the output
- * dtype.  The block dot products are exact for m <= 4; for larger m with fp16
- * x and k a multiple of 512 they come from fp16 matrix cores fed the codes as
- * fp16 subnormals, within about 1e-6 of exact relative to their magnitude
- * sum.  Streams each packed byte from memory once per call. */
+ * 1 <= m <= Q4_GEMV_MAX_M (the page's batched decode stage).  x is Q4_F32,
+ * Q4_F16 or Q4_BF16, y is Q4_F32 or Q4_F16.  Every output is the fp32 sum
+ * over blocks of d times the block dot product of x with (q - 8), rounded
+ * once to the output dtype.  The block dot products are exact for m <= 4;
+ * for larger m with fp16 x and k a multiple of 512 they come from fp16 matrix
+ * cores fed the codes as fp16 subnormals, within about 1e-6 of exact relative
+ * to their magnitude sum.  bf16 x with k a multiple of 512 is converted to
+ * fp16 inside the kernel (round to nearest even) and then takes the fp16
+ * path: exact for every bf16 value fp16 represents, which includes every
+ * value with 2^-14 <= |x| <= 65504 (larger magnitudes overflow; smaller ones
+ * are rounded to fp16's subnormal grid); other bf16 shapes are widened
+ * exactly to fp32.  Streams each packed byte from memory once per call. */
 q4_status q4_gemv(const void *x, int x_dtype, const void *packed, void *y,
                   int y_dtype, int64_t m, int64_t n, int64_t k,
                   q4_stream_t stream);
 
-/* Bytes of workspace q4_gemm needs for this shape (0 when none). */
+/* Bytes of workspace q4_gemm needs for this shape with fp16 activations (0
+ * when none). */
 size_t q4_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
+
+/* As q4_gemm_workspace_size for activations of dtype x_dtype (Q4_F16 or
+ * Q4_BF16; 0 for any other dtype or an invalid shape).  bf16 activations add
+ * m * k * 2 bytes (rounded up to 256), where they are staged as fp16. */
+size_t q4_gemm_workspace_size_dt(int64_t m, int64_t n, int64_t k, int x_dtype);
 
 /* Prefill GEMM: y[m][n] = x[m][k] . dequant(packed)^T for any m >= 1 (the
  * page's GPU path onto matrix cores): weight tiles are dequantised to fp16
@@ -125,10 +138,14 @@ size_t q4_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
  * accumulation.  Because the weights are rounded to fp16, every block scale
  * must satisfy |d| <= 8188 (every dequantised weight within the fp16 range,
  * |w| <= 65504); larger scales give infinite outputs (not checked; q4_gemv has
- * no such limit).  x must be Q4_F16; y is Q4_F32 or Q4_F16.  `workspace` must
- * hold q4_gemm_workspace_size(m, n, k) bytes (it may be NULL when that is
- * 0); its contents on entry are ignored.  A prompt processed in row chunks
- * passes x + c*rows*k and y + c*rows*n for chunk c. */
+ * no such limit).  x is Q4_F16 or Q4_BF16; y is Q4_F32 or Q4_F16.  bf16
+ * activations are first converted to fp16 into the workspace (round to
+ * nearest even; exact for every value fp16 represents, every value with
+ * 2^-14 <= |x| <= 65504 among them).  `workspace` must hold
+ * q4_gemm_workspace_size_dt(m, n, k, x_dtype) bytes (it may be NULL when that
+ * is 0) and must not overlap x, y or packed; its contents on entry are
+ * ignored.  A prompt processed in row chunks passes x + c*rows*k and
+ * y + c*rows*n for chunk c. */
 q4_status q4_gemm(const void *x, int x_dtype, const void *packed, void *y,
                   int y_dtype, int64_t m, int64_t n, int64_t k,
                   void *workspace, size_t workspace_bytes,

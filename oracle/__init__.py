@@ -4,6 +4,7 @@ from .q4_0 import (  # noqa: F401
     QK,
     BLOCK_BYTES,
     packed_size,
+    widen_bf16,
     quantize,
     unpack,
     dequantize,

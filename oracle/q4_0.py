@@ -63,6 +63,21 @@ def packed_size(n: int, k: int) -> int:
     return n * (k // QK) * BLOCK_BYTES
 
 
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> the values they denote, as fp32.
+
+    A bfloat16 value is the upper half of an IEEE binary32 pattern (sign, the
+    8-bit exponent, the top 7 fraction bits), so appending 16 zero bits gives
+    the same value in binary32 exactly.  bf16 weights and activations enter
+    the oracle through this widening; the quantiser and matmul definitions
+    below then apply unchanged.
+    """
+    b = np.asarray(bits)
+    if b.dtype != np.uint16:
+        raise TypeError(f"bf16 patterns must be uint16, got {b.dtype}")
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
 def _as_f32(w: np.ndarray) -> np.ndarray:
     """fp16 widens to fp32 exactly; fp32 passes through."""
     if w.dtype == np.float16:

@@ -18,6 +18,7 @@ from .inputs import (  # noqa: F401
     workload_activations,
     random_weights,
     random_activations,
+    bf16_bits,
     edge_case_weights,
     sha256_of,
 )

@@ -173,11 +173,23 @@ def random_weights(seed: int, n: int, k: int, dist: str = "normal") -> np.ndarra
     raise ValueError(dist)
 
 
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 draws rounded to bfloat16 (nearest even), as uint16 bit patterns:
+    how bf16 inputs are made from the fp32 draws (finite values only)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
 def random_activations(seed: int, m: int, k: int, dtype: str = "f16") -> np.ndarray:
+    """N(0, 1) activations: fp32, rounded to fp16, or rounded to bf16 and
+    returned as uint16 bit patterns ("bf16")."""
     rng = rng_for(seed, 0, 2 + m * 11 + k * 17)
     x = rng.standard_normal((m, k), dtype=np.float32)
     if dtype == "f16":
         return np.ascontiguousarray(x.astype(np.float16))
+    if dtype == "bf16":
+        return bf16_bits(x)
     return x
 
 

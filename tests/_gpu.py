@@ -10,6 +10,13 @@ def to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
+def to_dev_bf16(bits, dev):
+    """uint16 bfloat16 patterns -> a torch.bfloat16 device tensor (same bits)."""
+    import torch
+    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(a).view(torch.bfloat16).to(dev)
+
+
 def to_host(t):
     import torch
     torch.cuda.synchronize()

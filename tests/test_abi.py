@@ -11,7 +11,7 @@ ROOT = Path(__file__).resolve().parent.parent
 HEADER = ROOT / "include" / "q4.h"
 
 OK, INVALID, SHAPE, DTYPE, ALIGN, HIP, WORKSPACE = range(7)
-F32, F16 = 0, 1
+F32, F16, BF16 = 0, 1, 2
 A = 0x10000          # stand-in, 16-byte aligned "device" addresses: never dereferenced
 B = 0x20000000
 C = 0x40000000
@@ -60,7 +60,7 @@ def test_quantize_argument_checks(q4lib):
     assert f(A, F32, 0, 32, B, None) == SHAPE
     assert f(A, F32, 4, 48, B, None) == SHAPE
     assert f(A, F32, 4, 0, B, None) == SHAPE
-    assert f(A, 2, 4, 32, B, None) == DTYPE
+    assert f(A, 3, 4, 32, B, None) == DTYPE
     assert f(A + 4, F32, 4, 32, B, None) == ALIGN
     assert f(A, F32, 4, 32, B + 2, None) == ALIGN
     assert f(A, F32, 4, 32, A + 256, None) == INVALID      # packed inside w
@@ -78,6 +78,8 @@ def test_gemv_argument_checks(q4lib):
     assert f(A, F16, B, C, F16, 1, 8, 40, None) == SHAPE
     assert f(A, 5, B, C, F16, 1, 8, 32, None) == DTYPE
     assert f(A, F16, B, C, -1, 1, 8, 32, None) == DTYPE
+    assert f(A, F16, B, C, BF16, 1, 8, 32, None) == DTYPE    # outputs are fp32 or fp16
+    assert f(A, 3, B, C, F16, 1, 8, 32, None) == DTYPE
     assert f(A + 2, F16, B, C, F16, 1, 8, 32, None) == ALIGN
     assert f(A, F16, B + 8, C, F16, 1, 8, 32, None) == ALIGN
     assert f(A, F16, B, C + 1, F16, 1, 8, 32, None) == ALIGN
@@ -96,6 +98,16 @@ def test_gemm_argument_checks(q4lib):
     need = q4lib.q4_gemm_workspace_size(64, 8, 32)
     assert need >= 0
     assert q4lib.q4_gemm_workspace_size(0, 8, 32) == 0
+    # bf16 activations are staged as fp16 in the workspace
+    needb = q4lib.q4_gemm_workspace_size_dt(64, 8, 32, BF16)
+    assert needb >= need + 64 * 32 * 2
+    assert q4lib.q4_gemm_workspace_size_dt(64, 8, 32, F16) == need
+    assert q4lib.q4_gemm_workspace_size_dt(64, 8, 32, F32) == 0
+    assert f(A, BF16, B, C, F16, 64, 8, 32, None, 0, None) == WORKSPACE
+    assert f(A, BF16, B, C, F16, 64, 8, 32, 0x60000000, needb - 1, None) == WORKSPACE
+    assert f(A, BF16, B, C, F16, 64, 8, 32, 0x60000008, needb, None) == ALIGN
+    assert f(A, BF16, B, C, F16, 64, 8, 32, A, needb, None) == INVALID    # workspace over x
+    assert f(A, BF16, B, C, BF16, 64, 8, 32, 0x60000000, needb, None) == DTYPE
 
 
 def test_binding_fails_loudly_without_library(q4lib, monkeypatch, tmp_path):

@@ -7,7 +7,8 @@ import pytest
 
 import oracle
 import synth
-from _gpu import assert_matmul_close, sample_rows, to_dev, to_host, workload_weights_cached
+from _gpu import (assert_matmul_close, sample_rows, to_dev, to_dev_bf16, to_host,
+                  workload_weights_cached)
 
 pytestmark = pytest.mark.gpu
 
@@ -178,3 +179,41 @@ def test_slice_k_tiles(q4lib, gpu, m, n, k):
     packed = oracle.quantize(w)
     g = run_gemm(q4lib, x, packed, n, k, "f32", gpu)
     assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(37, 70, 96), (64, 300, 1024), (256, 1000, 2048),
+                                   (300, 11000, 1024), (1030, 2100, 1024)])
+def test_bf16_activations(q4lib, gpu, m, n, k):
+    """bf16 activations staged as fp16 in the workspace, then every GEMM path:
+    the output-split kernel (k % 64 != 0), slice-K tiles, 256 x 256 tiles with
+    a split-K tail; sampled rows for the larger shapes."""
+    import torch
+    w = synth.random_weights(5 * m + n + k, n, k, "student_t")
+    xb = synth.random_activations(3 * m + k, m, k, "bf16")
+    packed = oracle.quantize(w)
+    need16 = q4lib.q4_gemm_workspace_size(m, n, k)
+    needb = q4lib.q4_gemm_workspace_size_dt(m, n, k, q4lib.Q4_BF16)
+    assert needb >= need16 + m * k * 2
+    y = to_host(q4lib.q4_gemm(to_dev_bf16(xb, gpu), to_dev(packed, gpu), y_dtype=torch.float32,
+                              n=n, k=k))
+    rows = sample_rows(m, 96, m + n)
+    x = oracle.widen_bf16(xb)
+    assert_matmul_close(y[rows], x[rows], packed, n, k, what=f"bf16 m{m} n{n} k{k}")
+
+
+def test_bf16_chunked_matches_oracle(q4lib, gpu):
+    """Row chunks of a bf16 prompt by pointer offset, one shared workspace."""
+    import torch
+    m, n, k, cs = 512, 2048, 2048, 128
+    w = synth.random_weights(77, n, k, "normal")
+    xb = synth.random_activations(78, m, k, "bf16")
+    packed_d = to_dev(oracle.quantize(w), gpu)
+    xd = to_dev_bf16(xb, gpu)
+    y = torch.empty((m, n), dtype=torch.float16, device=gpu)
+    ws = torch.empty(q4lib.q4_gemm_workspace_size_dt(cs, n, k, q4lib.Q4_BF16), dtype=torch.uint8,
+                     device=gpu)
+    for c in range(m // cs):
+        q4lib.q4_gemm(xd[c * cs:(c + 1) * cs], packed_d, y=y[c * cs:(c + 1) * cs], workspace=ws)
+    rows = sample_rows(m, 64, 5)
+    assert_matmul_close(to_host(y)[rows], oracle.widen_bf16(xb)[rows], to_host(packed_d), n, k,
+                        what="bf16 chunks")

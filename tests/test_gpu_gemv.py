@@ -7,7 +7,7 @@ import pytest
 import oracle
 import synth
 from _golden import load
-from _gpu import assert_matmul_close, to_dev, to_host, workload_weights_cached
+from _gpu import assert_matmul_close, to_dev, to_dev_bf16, to_host, workload_weights_cached
 
 pytestmark = pytest.mark.gpu
 
@@ -236,3 +236,53 @@ def test_matrix_core_tile_rows_spread(q4lib, gpu, m, n, k):
     packed = oracle.quantize(w)
     g = run_gemv(q4lib, x, packed, n, k, "f32", gpu)
     assert_matmul_close(g, x, packed, n, k, what=f"m{m} n{n} k{k}")
+
+
+# bf16 activations: the m <= 4 kernel (k a multiple of 512) converts the
+# staged rows in LDS, the tile kernel (m > 4, k a multiple of 512) converts
+# each operand fragment, other shapes widen them exactly in the general kernel.
+BF16_CASES = [(1, 300, 2048), (2, 129, 5120), (3, 64, 512), (4, 1000, 17408),
+              (5, 4097, 1536), (16, 1000, 3072), (17, 520, 2048), (32, 16, 3072),
+              (1, 257, 1056), (13, 70, 768), (32, 7, 96), (4, 300, 2080)]
+
+
+@pytest.mark.parametrize("m,n,k", BF16_CASES)
+@pytest.mark.parametrize("ydt", ["f16", "f32"])
+def test_bf16_activations(q4lib, gpu, m, n, k, ydt):
+    import torch
+    w = synth.random_weights(3 * m + n + k, n, k, "student_t")
+    xb = synth.random_activations(7 * m + k, m, k, "bf16")
+    packed = oracle.quantize(w)
+    y = q4lib.q4_gemv(to_dev_bf16(xb, gpu), to_dev(packed, gpu),
+                      y_dtype=torch.float16 if ydt == "f16" else torch.float32, n=n, k=k)
+    assert_matmul_close(to_host(y), oracle.widen_bf16(xb), packed, n, k,
+                        what=f"bf16 m{m} n{n} k{k} -> {ydt}")
+
+
+@pytest.mark.parametrize("m,k", [(4, 512), (32, 512), (32, 96)])
+def test_bf16_one_hot_rows_give_exact_weights(q4lib, gpu, m, k):
+    """bf16 x = identity rows: y is the dequantised weight exactly, on each path."""
+    n = 70
+    w = synth.random_weights(31, n, k, "student_t")
+    packed = oracle.quantize(w)
+    deq = oracle.dequantize(packed, n, k)
+    x = np.zeros((m, k), np.float32)
+    x[np.arange(m), np.arange(m)] = 1
+    y = to_host(q4lib.q4_gemv(to_dev_bf16(synth.bf16_bits(x), gpu), to_dev(packed, gpu), n=n, k=k))
+    assert y.dtype == np.float32  # bf16 activations default to an fp32 output
+    assert np.array_equal(y, deq[:, :m].T)
+
+
+@pytest.mark.parametrize("m", [3, 10])
+def test_bf16_activations_across_the_fp16_range(q4lib, gpu, m):
+    """bf16 values spanning fp16's normal range (2^-14 .. 60000): the in-kernel
+    conversion is exact there, so the result stays within tolerance."""
+    n, k = 200, 1024
+    rng = np.random.default_rng(m)
+    mag = np.exp2(rng.uniform(-14, 15.8, size=(m, k))).astype(np.float32)
+    x = np.where(rng.random((m, k)) < 0.5, -mag, mag).astype(np.float32)
+    xb = synth.bf16_bits(x)
+    w = synth.random_weights(33, n, k, "normal") * np.float32(1e-3)
+    packed = oracle.quantize(w)
+    y = to_host(q4lib.q4_gemv(to_dev_bf16(xb, gpu), to_dev(packed, gpu), n=n, k=k))
+    assert_matmul_close(y, oracle.widen_bf16(xb), packed, n, k, what=f"bf16 range m{m}")

@@ -97,3 +97,21 @@ def test_codes_at_rounding_boundaries(q4lib, gpu, dt):
     want = oracle.quantize(w)
     bad = np.nonzero(np.any(got.reshape(-1, 18) != want.reshape(-1, 18), axis=1))[0]
     assert bad.size == 0, f"{bad.size} blocks differ, first {bad[:5]}"
+
+
+@pytest.mark.parametrize("n,k", [(3, 96), (17, 512), (64, 5120), (33, 2080)])
+@pytest.mark.parametrize("dist", ["normal", "student_t"])
+def test_bf16_weights(q4lib, gpu, n, k, dist):
+    """bf16 weights are widened exactly to fp32 and quantised by the same rule."""
+    from _gpu import to_dev_bf16
+    wb = synth.bf16_bits(synth.random_weights(n + 2 * k, n, k, dist))
+    got = to_host(q4lib.q4_quantize(to_dev_bf16(wb, gpu)))
+    assert np.array_equal(got, oracle.quantize(oracle.widen_bf16(wb)))
+
+
+def test_bf16_edge_case_weights(q4lib, gpu):
+    from _gpu import to_dev_bf16
+    n, k = 96, 32 * 24
+    wb = synth.bf16_bits(synth.edge_case_weights(7, n, k))
+    got = to_host(q4lib.q4_quantize(to_dev_bf16(wb, gpu)))
+    assert np.array_equal(got, oracle.quantize(oracle.widen_bf16(wb)))

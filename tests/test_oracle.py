@@ -14,6 +14,7 @@ The oracle is checked against things other than itself:
     must make at least one pin fail.
 """
 
+import math
 from fractions import Fraction as Fr
 
 import numpy as np
@@ -294,6 +295,64 @@ def test_exact_rational_dot_products(xdt):
                         sacc += abs(term)
             assert abs(Fr(float(y[mi, ni])) - acc) <= Fr(1, 10 ** 12) * max(sacc, Fr(1))
             assert abs(Fr(float(S[mi, ni])) - sacc) <= Fr(1, 10 ** 12) * max(sacc, Fr(1))
+
+
+# ---------------------------------------------------------------- bf16 inputs
+
+def _bf16_by_fields(bits: int) -> float:
+    """The value a bfloat16 pattern denotes, decoded field by field (sign, 8-bit
+    biased exponent, 7-bit fraction; exponent 0 is subnormal, 255 inf/nan)."""
+    sign = -1.0 if bits >> 15 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return sign * float("inf") if f == 0 else float("nan")
+    if e == 0:
+        return sign * math.ldexp(f, -126 - 7)
+    return sign * math.ldexp(128 + f, e - 127 - 7)
+
+
+@pytest.mark.parametrize("bits,value", [
+    (0x3F80, 1.0), (0xC000, -2.0), (0x4049, 3.140625), (0x3E80, 0.25), (0x4480, 1024.0),
+    (0x477F, 65280.0), (0x0001, 2.0 ** -133), (0x0080, 2.0 ** -126), (0x7F7F, 255 * 2.0 ** 120),
+    (0x0000, 0.0), (0xBF81, -1.0078125)])
+def test_bf16_widening_known_values(bits, value):
+    v = oracle.widen_bf16(np.array([bits], np.uint16))[0]
+    assert v.dtype == np.float32 and float(v) == value
+
+
+def test_bf16_widening_every_pattern():
+    """All 65536 patterns against a field-by-field decoding; -0 keeps its sign."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns
+        got = oracle.widen_bf16(bits).astype(np.float64)
+    want = np.array([_bf16_by_fields(int(b)) for b in bits])
+    finite = np.isfinite(want)
+    assert np.array_equal(got[finite], want[finite])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(np.isinf(got), np.isinf(want))
+    assert np.signbit(oracle.widen_bf16(np.array([0x8000], np.uint16))[0])
+
+
+def test_exact_rational_dot_products_bf16():
+    """bf16 activations: the oracle's sums against exact rational sums of the
+    field-decoded activation values and the byte-decoded weights."""
+    m, n, k = 2, 4, 64
+    w = synth.random_weights(14, n, k, "student_t")
+    xb = synth.random_activations(15, m, k, "bf16")
+    packed = oracle.quantize(w)
+    y, S = oracle.matmul_ref(oracle.widen_bf16(xb), packed, n, k)
+    raw = packed.reshape(n, k // 32, 18)
+    for mi in range(m):
+        for ni in range(n):
+            acc = Fr(0)
+            for b in range(k // 32):
+                d = Fr(float(raw[ni, b, :2].view("<f2")[0]))
+                for i in range(16):
+                    byte = int(raw[ni, b, 2 + i])
+                    for e, q in ((i, byte & 0xF), (i + 16, byte >> 4)):
+                        acc += Fr(_bf16_by_fields(int(xb[mi, b * 32 + e]))) * (q - 8) * d
+            assert abs(Fr(float(y[mi, ni])) - acc) <= Fr(1, 10 ** 12) * max(abs(acc), Fr(1))
 
 
 def test_check_bound():

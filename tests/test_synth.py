@@ -60,3 +60,25 @@ def test_edge_cases_cover_every_pattern():
     assert np.all(blocks[1] == 0) and not np.any(np.signbit(blocks[1]))
     assert np.all(blocks[2] == 0) and np.all(np.signbit(blocks[2]))
     assert np.all(np.isfinite(w)) and np.abs(w).max() < 65520 * 8
+
+
+def test_bf16_bits_round_to_nearest_even():
+    """bf16 inputs are the fp32 draws rounded to nearest even: exact values,
+    ties to the even pattern, and random values against exact rational
+    rounding."""
+    from fractions import Fraction as Fr
+    cases = {1.0: 0x3F80, -2.0: 0xC000, 1.0 + 2.0 ** -8: 0x3F80, 1.0 + 3 * 2.0 ** -8: 0x3F82,
+             1.0 + 2.0 ** -8 + 2.0 ** -20: 0x3F81, 65504.0: 0x4780}
+    got = synth.bf16_bits(np.array(list(cases), np.float32))
+    assert [int(v) for v in got] == list(cases.values())
+    x = np.random.default_rng(0).standard_normal(2000).astype(np.float32)
+    b = synth.bf16_bits(x)
+    for xv, bv in zip(x, b):
+        # neighbouring patterns bracket x; the chosen one is nearest (even on ties)
+        lo = int(bv)
+        val = (np.array([lo], np.uint32) << 16).view(np.float32)[0]
+        err = abs(Fr(float(xv)) - Fr(float(val)))
+        for nb in (lo - 1, lo + 1):
+            other = (np.array([nb], np.uint32) << 16).view(np.float32)[0]
+            e2 = abs(Fr(float(xv)) - Fr(float(other)))
+            assert err < e2 or (err == e2 and lo % 2 == 0)
