@@ -551,12 +551,15 @@ def traffic_summary(fetch_csv, write_csv, out_path):
     return data
 
 
-def trace_summary(trace_csv, steps):
+def trace_summary(trace_csv, steps, warmup):
     """Per batch size, the mean duration of the GEMV dispatches that bench_gemv
-    times, from a rocprofv3 kernel-trace CSV of a default run: the last
-    3 steps len(ms) GEMV dispatches are, per batch size in WORKLOADS[2].ms
-    order, `steps` eager launches (capture), `steps` in the warm replay and
-    `steps` in the timed replay."""
+    times, from a rocprofv3 kernel-trace CSV of a run with the same steps and
+    warmup.  bench_gemv is the run's first GEMV work: (2 max(warmup, 1) +
+    2 steps) len(ms) dispatches for the whole-step graphs (eager capture runs,
+    then the replays), then per batch size in WORKLOADS[2].ms order `steps`
+    eager launches (capture), `steps` in the warm replay and `steps` in the
+    timed replay.  Later legs (layer decode, bf16) launch more GEMVs after
+    these."""
     import csv
     import synth
     ms = list(synth.WORKLOADS[2].ms)
@@ -569,7 +572,8 @@ def trace_summary(trace_csv, steps):
                 end = int(r.get("End_Timestamp") or r.get("End-Timestamp"))
                 rows.append((start, end - start, name))
     rows.sort()
-    tail = rows[-3 * steps * len(ms):]
+    first = (2 * max(warmup, 1) + 2 * steps) * len(ms)
+    tail = rows[first:first + 3 * steps * len(ms)]
     out = []
     for i, m in enumerate(ms):
         rep = tail[(3 * i + 2) * steps:(3 * i + 3) * steps]
@@ -625,7 +629,7 @@ def main():
     args = ap.parse_args()
 
     if args.trace_summary:
-        for r in trace_summary(args.trace_summary, args.steps):
+        for r in trace_summary(args.trace_summary, args.steps, args.warmup):
             print(json.dumps(r))
         return
     if args.traffic_summary:

@@ -41,10 +41,15 @@ in fp64 (every product of an fp16/fp32 activation and a dequantised weight is
 exact in fp64), together with ``S = sum |x * w|`` which scales the acceptance
 bound ``|gpu - y| <= 1e-3 * S + 1e-6``.
 
+bf16 inputs (weights or activations) enter through ``widen_bf16``, the exact
+widening of a bfloat16 pattern to binary32; everything after it is unchanged.
+
 Pins (in ``tests/test_oracle.py``): hand-worked blocks derived from the rule
 above (``tests/golden``), the round-trip bound ``|x - dequant| <= |d|/2`` on
 unclamped elements, code-range and maximum-element invariants, one-hot and
-all-ones activations, and exact rational brute-force dot products.
+all-ones activations, exact rational brute-force dot products (fp16, fp32
+and bf16 activations), and the bf16 widening against a field-by-field
+decoding of all 65536 patterns.
 """
 
 from __future__ import annotations
