@@ -23,6 +23,8 @@ The same JSON line carries:
                    launch on their concatenated packed rows);
   layer_prefill -- the same layer's GEMMs at M = 256 and 4096, seven launches
                    and four;
+  other_configs -- the 512 x 512 fp32 linear (latency: quantise, GEMV) and the
+                   17408 x 5120 gate/up weight with outlier blocks, m = 1, 10, 32;
   bf16          -- bf16 activations on the headline GEMV and the prefill GEMM;
   host_twin     -- the host-CPU twin (libq4host) on the same packed bytes,
                    on the host cores (a second backend, not a GPU figure);
@@ -446,6 +448,67 @@ def bench_bf16(q4, torch, dev, s, steps, gemm_reps):
             "gemm_workload": f"prefill_{m}x{n2}x{k2}, bf16 x, fp16 y", "gemm": gemm}
 
 
+def bench_other_configs(q4, torch, dev, steps, rotate_bytes):
+    """The two other single-linear configurations: the 512 x 512 linear with
+    fp32 activations and output (a latency figure: its 147 KB of packed
+    weights stay in L2, so one copy is reused), quantise and GEMV; and the
+    17408 x 5120 gate/up weight with 0.1% outlier blocks at m = 1, 10 and 32
+    (weights rotated over >= 1 GiB, weight GB/s against 8 TB/s)."""
+    import synth
+    out = {}
+    wl = synth.WORKLOADS[1]
+    lin = wl.linears[0]
+    w = torch.from_numpy(synth.workload_weights(wl, lin)).to(dev)
+    packed = q4.q4_quantize(w)
+    x = torch.from_numpy(synth.workload_activations(wl, lin.k, 1)).to(dev)
+    y = torch.empty((1, lin.n), dtype=torch.float32, device=dev)
+
+    def quant():
+        for _ in range(steps):
+            q4.q4_quantize(w, packed=packed)
+
+    def gemv():
+        for _ in range(steps):
+            q4.q4_gemv(x, packed, y=y)
+
+    row = {}
+    for name, fn in (("quantize_us", quant), ("gemv_us", gemv)):
+        g = capture(torch, fn)
+        g.replay()
+        row[name] = replay_seconds(torch, g) / steps * 1e6
+        del g
+    out[wl.name] = {"n": lin.n, "k": lin.k, "m": 1, "x_dtype": "f32", "y_dtype": "f32", **row}
+
+    wl = synth.WORKLOADS[3]
+    lin = wl.linears[0]
+    n, k = lin.n, lin.k
+    wbytes = n * (k // QK) * BLOCK_BYTES
+    wd = torch.from_numpy(synth.workload_weights(wl, lin)).to(dev)
+    ncopies = max(2, -(-rotate_bytes // wbytes))
+    copies = [q4.q4_quantize(wd) for _ in range(ncopies)]
+    del wd
+    xs = torch.from_numpy(synth.workload_activations(wl, k, max(wl.ms))).to(dev)
+    per_m = []
+    for m in wl.ms:
+        y = torch.empty((m, n), dtype=torch.float16, device=dev)
+        reps = min(steps, 100)
+
+        def fn(m=m, y=y, reps=reps):
+            for i in range(reps):
+                q4.q4_gemv(xs[:m], copies[i % ncopies], y=y)
+
+        g = capture(torch, fn)
+        g.replay()
+        t = replay_seconds(torch, g) / reps
+        del g
+        alg = gemv_alg_bytes(m, n, k)
+        per_m.append({"m": m, "mean_us": t * 1e6, "alg_gbs": alg / t / 1e9,
+                      "frac_hbm": alg / t / 1e9 / HBM_PEAK_GBS})
+    out[wl.name] = {"n": n, "k": k, "weight_copies_rotated": ncopies, "per_m": per_m}
+    del copies
+    return out
+
+
 # ------------------------------------------------------------ HBM traffic
 
 TRAFFIC_CALIB_BYTES = 512 << 20
@@ -618,7 +681,8 @@ def main():
     ap.add_argument("--rotate-mib", type=int, default=1024)
     ap.add_argument("--gemm-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "gemv", "gemm", "quantize", "layer", "host", "bf16"],
+    ap.add_argument("--only", choices=["all", "gemv", "gemm", "quantize", "layer", "host", "bf16",
+                                       "other"],
                     default="all")
     ap.add_argument("--traffic", action="store_true",
                     help="run the launches the FETCH_SIZE / WRITE_SIZE counter passes read")
@@ -680,6 +744,8 @@ def main():
     if args.only in ("all", "layer"):
         out["layer_decode"] = bench_layer_decode(q4, torch, dev, min(args.steps, 50), rotate)
         out["layer_prefill"] = bench_layer_prefill(q4, torch, dev, 3)
+    if args.only in ("all", "other"):
+        out["other_configs"] = bench_other_configs(q4, torch, dev, args.steps, rotate)
     if args.only in ("all", "bf16"):
         out["bf16"] = bench_bf16(q4, torch, dev, g["setup"], args.steps, args.gemm_reps)
     if args.only in ("all", "host"):

@@ -55,8 +55,11 @@ __device__ __forceinline__ void unroll(F&& f) {
 
 // Geometry of one phase slot for T row tiles, AT activation tiles, PB blocks
 // per phase, NW computing waves and NP copying waves (NP = 0: the computing
-// waves copy too).
-template <int T, int AT, int PB, int NW, int NP>
+// waves copy too).  WR (<= 16 T) is the weight rows a slot holds: below 16 T
+// the last tile's rows past WR read bytes of the slot's activation area
+// (in bounds; they feed only outputs that are never stored), which lets
+// three slots of 5 tiles x 2 activation tiles fit the LDS.
+template <int T, int AT, int PB, int NW, int NP, int WR = 16 * T>
 struct TileGeo {
   static constexpr int nw = NW;
   static constexpr int lanes = (NW + NP) * kWave;         // threads of the workgroup
@@ -66,7 +69,8 @@ struct TileGeo {
   static constexpr int row_pc = PB * kBlockBytes / 16;    // weight pieces per row
   static constexpr int wstride_pc = row_pc + 1;           // odd row stride (pieces)
   static constexpr int wstride = 16 * wstride_pc;
-  static constexpr int wpos = 16 * T * wstride_pc;        // weight pieces per slot
+  static_assert(WR >= 1 && WR <= 16 * T, "weight rows of a slot");
+  static constexpr int wpos = WR * wstride_pc;             // weight pieces per slot
   static constexpr int niw = (wpos + clanes - 1) / clanes;  // copy rounds (max per wave)
   static constexpr int wbytes = (16 * wpos + 255) / 256 * 256;
   static constexpr int xp = PB * kQK * 2 / 16;            // 16-byte pieces per activation row
@@ -92,11 +96,12 @@ struct TileGeo {
 // the copying waves convert their own pieces in LDS before the phase barrier
 // instead measured slower: 12.3 against 8.9 us at 5120 x 5120, m = 16, as it
 // delays the barrier and the next phase's copies.)
-template <int T, int AT, int PB, bool FULL, int NW, int NP, bool XB>
+template <int T, int AT, int PB, bool FULL, int NW, int NP, bool XB, int WR>
 __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, void* __restrict__ y, int m,
     int64_t n, int64_t k, int y_f16, int rows) {
-  using G = TileGeo<T, AT, PB, NW, NP>;
+  using G = TileGeo<T, AT, PB, NW, NP, WR>;
+  static_assert(!FULL || WR == 16 * T, "a full workgroup copies 16 T rows");
   constexpr int CW = G::cwaves;
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
   const int lane = threadIdx.x & (kWave - 1);
@@ -328,12 +333,13 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
   }
 }
 
-template <int T, int AT, int PB, bool FULL, bool XB, int NW = 8, int NP = 4>
+template <int T, int AT, int PB, bool FULL, bool XB, int WR = 16 * T, int NW = 8, int NP = 4>
 hipError_t launch_tile_f(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
                          int64_t n, int64_t k, int rows, hipStream_t s) {
-  using G = TileGeo<T, AT, PB, NW, NP>;
+  using G = TileGeo<T, AT, PB, NW, NP, WR>;
   static_assert(G::lds <= kTLdsMax, "LDS budget");
-  const void* fn = reinterpret_cast<const void*>(&gemv_tile_kernel<T, AT, PB, FULL, NW, NP, XB>);
+  const void* fn =
+      reinterpret_cast<const void*>(&gemv_tile_kernel<T, AT, PB, FULL, NW, NP, XB, WR>);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     const hipError_t e =
@@ -341,7 +347,7 @@ hipError_t launch_tile_f(const void* x, const uint8_t* packed, void* y, bool y_f
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  if (rows < 1 || rows > 16 * T) return hipErrorInvalidValue;
+  if (rows < 1 || rows > WR) return hipErrorInvalidValue;
   const int64_t grid = (n + rows - 1) / rows;
   const half_t* xp = static_cast<const half_t*>(x);
   int yf = y_f16 ? 1 : 0;
@@ -362,6 +368,10 @@ struct TilePlan {
   int T, AT, PB, rows;
 };
 
+// Five row tiles with two activation tiles (m > 16) fit the LDS ring only
+// with at most this many weight rows per slot.
+constexpr int kT5AT2Rows = 68;
+
 // Rows per workgroup: whole 16-row tiles, enough for one workgroup per
 // compute unit (capped where the LDS ring would not fit; larger matrices take
 // several rounds).  With K long enough for eight or more phases the rows are
@@ -376,6 +386,7 @@ TilePlan tile_plan(int m, int64_t n, int64_t k) {
   const int tmax = p.AT == 1 ? 5 : 4;
   int64_t tfull = ((n + 15) / 16 + cu - 1) / cu;
   if (tfull < 1) tfull = 1;
+  const bool wide = tfull > tmax;
   if (tfull > tmax) tfull = tmax;
   p.PB = p.AT == 1 && tfull <= 2 && k % 1024 == 0 ? 32 : 16;
   int64_t rows = 16 * tfull;
@@ -383,6 +394,13 @@ TilePlan tile_plan(int m, int64_t n, int64_t k) {
   if (nph >= 8) {
     const int64_t spread = (n + cu - 1) / cu;
     if (spread < rows) rows = spread;
+  }
+  // m > 16 with more than 64 rows per compute unit: up to 68 rows in five
+  // tiles (a slot sized for 68 weight rows) keeps 17408 rows in one round of
+  // 256 workgroups instead of 272 (a second round for the last 16).
+  if (p.AT == 2 && wide) {
+    const int64_t spread = (n + cu - 1) / cu;
+    rows = spread < kT5AT2Rows ? spread : kT5AT2Rows;
   }
   p.rows = static_cast<int>(rows);
   p.T = static_cast<int>((rows + 15) / 16);
@@ -400,6 +418,9 @@ hipError_t launch_tile_tt(const TilePlan& p, const void* x, const uint8_t* packe
     default:
       if constexpr (AT == 1 && PB == 16)
         return launch_tile_t<5, AT, PB, XB>(x, packed, y, y_f16, m, n, k, p.rows, s);
+      if constexpr (AT == 2 && PB == 16)
+        return launch_tile_f<5, 2, 16, false, XB, kT5AT2Rows>(x, packed, y, y_f16, m, n, k,
+                                                              p.rows, s);
       return hipErrorInvalidValue;
   }
 }

@@ -286,3 +286,18 @@ def test_bf16_activations_across_the_fp16_range(q4lib, gpu, m):
     packed = oracle.quantize(w)
     y = to_host(q4lib.q4_gemv(to_dev_bf16(xb, gpu), to_dev(packed, gpu), n=n, k=k))
     assert_matmul_close(y, oracle.widen_bf16(xb), packed, n, k, what=f"bf16 range m{m}")
+
+
+@pytest.mark.parametrize("m,n,k", [(32, 17408, 1024), (17, 20000, 512), (24, 34816, 1024)])
+def test_matrix_core_tile_wide_two_activation_tiles(q4lib, gpu, m, n, k):
+    """m > 16 with more than 64 rows per compute unit: five row tiles in a slot
+    sized for 68 weight rows (the fifth tile's rows past 68 read bytes of the
+    activation area and are never stored); 34816 rows take two rounds."""
+    w = synth.random_weights(23 * m + n + k, n, k, "student_t")
+    x = synth.random_activations(29 * m + k, m, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemv(q4lib, x, packed, n, k, "f32", gpu)
+    rng = np.random.default_rng(n)
+    cols = np.unique(np.concatenate([rng.choice(n, size=1500, replace=False),
+                                     np.arange(0, n, 68), np.arange(67, n, 68), [n - 1]]))
+    assert_matmul_close(g[:, cols], x, packed, n, k, cols=cols, what=f"wide m{m} n{n} k{k}")
