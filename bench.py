@@ -62,6 +62,8 @@ CHUNK_ROWS = (128, 256, 512)     # prefill chunk-size sweep over the 2048-row ba
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in sorted((ROOT / "bit_block_quantized_q4_amd" / "csrc").glob("*")):
+        if p.suffix not in (".hip", ".hpp", ".h"):
+            continue  # sources only (not compiler by-products left beside them)
         h.update(p.name.encode())
         h.update(p.read_bytes())
     return h.hexdigest()[:16]
