@@ -654,10 +654,17 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
 
 constexpr int64_t kLdsMax = 160 * 1024;
 constexpr int kBalP = 4;  // tasks in flight per wave
+// Two tasks in flight per wave where four do not leave room in LDS for the
+// staged activations (m = 4 at k = 17408: 139 KB of x), for workgroups of at
+// most 32 rows: measured 16.4 -> 14.8 us at 5120 x 17408, m = 4 (against the
+// tile kernel), but 32.7 -> 38.8 us at 16384 x 16384 (64 rows per workgroup,
+// too little in flight for that much work), which keeps the tile kernel.
+constexpr int kBalPSmall = 2;
+constexpr int kBalPSmallMaxGroups = 8;
 
 
 struct BalPlan {
-  int rows_per_wg = 0, grid = 0, nw = 0;
+  int rows_per_wg = 0, grid = 0, nw = 0, ring = 0;
   int64_t lds = 0;
 };
 
@@ -671,10 +678,13 @@ bool bal_plan(int m, int64_t n, int64_t k, BalPlan* p) {
   p->rows_per_wg = static_cast<int>(rows);
   p->grid = static_cast<int>((n + rows - 1) / rows);
   const int rg = static_cast<int>(rows / 4);
-  for (int nw : {8, 16}) {
-    const BalLds L = bal_lds(m, k, rg, nw, kBalP);
+  const int tries[3][2] = {{8, kBalP}, {16, kBalP}, {8, kBalPSmall}};  // {waves, ring}
+  for (const auto& t : tries) {
+    if (t[1] == kBalPSmall && rg > kBalPSmallMaxGroups) break;
+    const BalLds L = bal_lds(m, k, rg, t[0], t[1]);
     if (L.total <= kLdsMax) {
-      p->nw = nw;
+      p->nw = t[0];
+      p->ring = t[1];
       p->lds = L.total;
       return true;
     }
@@ -682,10 +692,10 @@ bool bal_plan(int m, int64_t n, int64_t k, BalPlan* p) {
   return false;
 }
 
-template <int NW, int MR, bool XB>
+template <int NW, int P, int MR, bool XB>
 hipError_t launch_bal_t(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
                         int64_t n, int64_t k, const BalPlan& p, hipStream_t s) {
-  const void* fn = reinterpret_cast<const void*>(&gemv_bal_kernel<NW, kBalP, MR, XB>);
+  const void* fn = reinterpret_cast<const void*>(&gemv_bal_kernel<NW, P, MR, XB>);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -703,8 +713,9 @@ hipError_t launch_bal_t(const void* x, const uint8_t* packed, void* y, bool y_f1
 template <int MR, bool XB>
 hipError_t dispatch_bal_m(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
                           int64_t n, int64_t k, const BalPlan& p, hipStream_t s) {
-  if (p.nw == 16) return launch_bal_t<16, MR, XB>(x, packed, y, y_f16, m, n, k, p, s);
-  return launch_bal_t<8, MR, XB>(x, packed, y, y_f16, m, n, k, p, s);
+  if (p.ring == kBalPSmall) return launch_bal_t<8, kBalPSmall, MR, XB>(x, packed, y, y_f16, m, n, k, p, s);
+  if (p.nw == 16) return launch_bal_t<16, kBalP, MR, XB>(x, packed, y, y_f16, m, n, k, p, s);
+  return launch_bal_t<8, kBalP, MR, XB>(x, packed, y, y_f16, m, n, k, p, s);
 }
 
 // MR: activation rows accumulated (m rounded up to 1, 2 or 4).

@@ -301,3 +301,15 @@ def test_matrix_core_tile_wide_two_activation_tiles(q4lib, gpu, m, n, k):
     cols = np.unique(np.concatenate([rng.choice(n, size=1500, replace=False),
                                      np.arange(0, n, 68), np.arange(67, n, 68), [n - 1]]))
     assert_matmul_close(g[:, cols], x, packed, n, k, cols=cols, what=f"wide m{m} n{n} k{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(4, 5120, 17408), (4, 300, 16384), (3, 1000, 17408), (4, 37, 17920)])
+def test_balanced_long_k(q4lib, gpu, m, n, k):
+    """m <= 4 with long K: the staged activations (up to 140 KB) leave room for
+    a two-task ring per wave only, which the plan then takes."""
+    w = synth.random_weights(41 * m + n + k, n, k, "outlier")
+    x = synth.random_activations(43 * m + k, m, k, "f16")
+    packed = oracle.quantize(w)
+    g = run_gemv(q4lib, x, packed, n, k, "f32", gpu)
+    cols = np.unique(np.concatenate([np.arange(0, n, 11), [n - 1]]))
+    assert_matmul_close(g[:, cols], x, packed, n, k, cols=cols, what=f"m{m} n{n} k{k}")
