@@ -196,7 +196,7 @@ def _check(status: int, what: str):
 
 
 def q4_quantize(w, packed=None, stream=None):
-    """Quantise a [n, k] fp32/fp16 device weight into a [n, k/32*18] uint8 tensor."""
+    """Quantise a [n, k] fp32/fp16/bf16 device weight into a [n, k/32*18] uint8 tensor."""
     torch = _torch()
     _need_device(w, "w")
     if w.dim() != 2:
@@ -234,7 +234,8 @@ def q4_gemv(x, packed, y=None, y_dtype=None, stream=None, n=None, k=None):
 
 
 def q4_gemm(x, packed, y=None, y_dtype=None, workspace=None, stream=None, n=None, k=None):
-    """Prefill GEMM y[m, n] = x[m, k] . dequant(W)^T on fp16 MFMA (x must be fp16)."""
+    """Prefill GEMM y[m, n] = x[m, k] . dequant(W)^T on fp16 MFMA (x fp16, or bf16
+    staged as fp16 in the workspace)."""
     torch = _torch()
     _need_device(x, "x")
     _need_device(packed, "packed")
