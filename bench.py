@@ -33,6 +33,8 @@ The same JSON line carries:
 Counter passes (HBM traffic): run `bench.py --traffic` once under
 `rocprofv3 --pmc FETCH_SIZE` and once under `--pmc WRITE_SIZE`, then
 `bench.py --traffic-summary FETCH.csv WRITE.csv` writes profiles/traffic.json.
+Matrix-core pass: `bench.py --mfma` under `rocprofv3 --pmc MfmaUtil MfmaFlopsF16`,
+then `bench.py --mfma-summary PMC.csv` writes profiles/mfma.json.
 
 Run: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -543,6 +545,54 @@ def traffic_run(q4, torch, dev, rotate_bytes, launches=20):
     print("traffic launches done", flush=True)
 
 
+def mfma_run(q4, torch, dev, reps=3):
+    """The launches the matrix-core counter pass (MfmaUtil, MfmaFlopsF16) reads:
+    the 2048 x 17408 x 5120 prefill as one launch and as 8 chunks of 256 rows."""
+    _, _, _, whole, chunked = gemm_setup(q4, torch, dev)
+    for _ in range(reps):
+        whole()
+    for _ in range(reps):
+        chunked(256)()
+    torch.cuda.synchronize()
+    print("mfma launches done", flush=True)
+
+
+def mfma_summary(csv_path, out_path):
+    """profiles/mfma.json from the counter pass over mfma_run: per GEMM kernel,
+    the median per dispatch of MfmaUtil (matrix-core busy cycles over the
+    dispatch's active cycles, all SIMDs) and of MfmaFlopsF16 (fp16 matrix
+    flops issued), with the algorithmic flops of the dispatch's share."""
+    import re
+    by = {}
+    for did, name, cnt, val in _pmc_rows(csv_path):
+        if "gemm_" not in name and "splitk_reduce" not in name:
+            continue
+        if "gemm_mfma_kernel" in name:
+            key = "gemm_mfma_256x256" if ("ILi256" in name or "<256" in name) else "gemm_mfma_128x128"
+        elif "gemm_slicek_kernel" in name:
+            key = "gemm_slicek_128x128"
+        elif "splitk_reduce" in name:
+            key = "splitk_reduce"
+        else:
+            key = "other_gemm"
+        # the output type is the kernels' last template argument: fp16 y, or
+        # fp32 split-K partials (the tail)
+        if re.search(r"kernelI(?:Li\d+E)*fE", name) or "float>" in name:
+            key += "_f32_partials"
+        else:
+            key += "_f16_out"
+        by.setdefault(key, {}).setdefault(cnt, []).append(val)
+    kernels = {}
+    for key, cnts in sorted(by.items()):
+        kernels[key] = {c: float(np.median(v)) for c, v in cnts.items()}
+        kernels[key]["dispatches"] = max(len(v) for v in cnts.values())
+    data = {"source_hash": kernel_source_hash(),
+            "workload": "prefill_2048x17408x5120, whole launch and 8 x 256-row chunks",
+            "peak_mfma_f16_tflops": MFMA_F16_PEAK_TFLOPS, "kernels": kernels}
+    Path(out_path).write_text(json.dumps(data, indent=1) + "\n")
+    return data
+
+
 def _pmc_rows(csv_path):
     """(dispatch id, kernel name, counter, value) rows of a rocprofv3 counter CSV."""
     import csv
@@ -690,6 +740,10 @@ def main():
                     help="run the launches the FETCH_SIZE / WRITE_SIZE counter passes read")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from the two counter passes")
+    ap.add_argument("--mfma", action="store_true",
+                    help="run the launches the MfmaUtil / MfmaFlopsF16 counter pass reads")
+    ap.add_argument("--mfma-summary", metavar="PMC_CSV",
+                    help="write profiles/mfma.json from that counter pass")
     ap.add_argument("--trace-summary", metavar="TRACE_CSV",
                     help="print per-batch-size GEMV durations from a kernel-trace CSV of a default run")
     args = ap.parse_args()
@@ -702,6 +756,9 @@ def main():
         d = traffic_summary(args.traffic_summary[0], args.traffic_summary[1],
                             ROOT / "profiles" / "traffic.json")
         print(json.dumps(d, indent=1))
+        return
+    if args.mfma_summary:
+        print(json.dumps(mfma_summary(args.mfma_summary, ROOT / "profiles" / "mfma.json"), indent=1))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -719,6 +776,9 @@ def main():
     rotate = args.rotate_mib << 20
     if args.traffic:
         traffic_run(q4, torch, dev, rotate)
+        return
+    if args.mfma:
+        mfma_run(q4, torch, dev)
         return
 
     out = {"metric": METRIC}
