@@ -86,6 +86,22 @@ def load_traffic(kernel_key: str):
     return data.get("kernels", {}).get(kernel_key)
 
 
+def load_mfma_util(kernel_key: str):
+    """Matrix-core busy percentage of a GEMM kernel from the committed counter
+    summary, or None when the kernels changed since it was taken."""
+    f = ROOT / "profiles" / "mfma.json"
+    if not f.exists():
+        return None
+    try:
+        data = json.loads(f.read_text())
+    except ValueError:
+        return None
+    if data.get("source_hash") != kernel_source_hash():
+        return None
+    k = data.get("kernels", {}).get(kernel_key)
+    return None if k is None else k.get("MfmaUtil")
+
+
 def capture(torch, fn):
     """fn's launches recorded into a HIP graph (one eager call first warms them)."""
     fn()
@@ -263,7 +279,8 @@ def bench_gemm(q4, torch, dev, reps):
         **res, "chunk_sweep": sweep,
         "roofline": {"bound": "mfma", "achieved": best, "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": best / MFMA_F16_PEAK_TFLOPS,
-                     "traffic": load_traffic("gemm_2048x17408x5120")},
+                     "traffic": load_traffic("gemm_2048x17408x5120"),
+                     "mfma_util_pct": load_mfma_util("gemm_mfma_256x256_f16_out")},
     }
 
 
