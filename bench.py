@@ -35,6 +35,9 @@ Counter passes (HBM traffic): run `bench.py --traffic` once under
 `bench.py --traffic-summary FETCH.csv WRITE.csv` writes profiles/traffic.json.
 Matrix-core pass: `bench.py --mfma` under `rocprofv3 --pmc MfmaUtil MfmaFlopsF16`,
 then `bench.py --mfma-summary PMC.csv` writes profiles/mfma.json.
+Wave-state pass: `bench.py --traffic` under `rocprofv3 --pmc` with the SQ
+counters of SQ_COUNTERS (and GRBM_GUI_ACTIVE), then `bench.py --sq-summary
+PMC.csv` writes profiles/sq.json.
 
 Run: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -625,40 +628,75 @@ def _pmc_rows(csv_path):
     return rows
 
 
+def _traffic_key(name):
+    """Workload of a dispatch in the traffic_run launches (None: not counted)."""
+    if "neg_kernel" in name:
+        return "calib_copy"
+    if "gemv_" in name and "_kernel" in name:
+        return "gemv"
+    if "quantize_kernel" in name:
+        return "quantize_fp32_5120x5120"
+    if "gemm_mfma_kernelILi256" in name or "gemm_mfma_kernel<256" in name:
+        return "gemm_2048x17408x5120"
+    return None
+
+
+def _traffic_groups(csv_path, counter):
+    """Per workload, the per-dispatch values of one counter of a traffic_run
+    pass.  GEMV dispatches are attributed to batch sizes by launch order
+    (traffic_run launches them in WORKLOADS[2].ms order)."""
+    import synth
+    ms = list(synth.WORKLOADS[2].ms)
+    by, gemv = {}, []
+    for did, name, cnt, val in _pmc_rows(csv_path):
+        if cnt != counter:
+            continue
+        key = _traffic_key(name)
+        if key == "gemv":
+            gemv.append(val)
+        elif key:
+            by.setdefault(key, []).append(val)
+    if gemv:
+        per = len(gemv) // len(ms)
+        for i, m in enumerate(ms):
+            by[f"gemv_5120x5120_m{m}"] = gemv[i * per:(i + 1) * per]
+    return by
+
+
+SQ_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+               "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT")
+
+
+def sq_summary(csv_path, out_path):
+    """profiles/sq.json from one counter pass of SQ_COUNTERS over traffic_run:
+    per workload, the median per dispatch of each counter, and the ratios read
+    from them (waiting cycles per wave cycle; LDS bank-conflict cycles per
+    cycle of LDS instruction activity)."""
+    kernels = {}
+    for c in SQ_COUNTERS:
+        for key, vals in _traffic_groups(csv_path, c).items():
+            if key == "calib_copy":
+                continue
+            kernels.setdefault(key, {})[c] = float(np.median(vals))
+            kernels[key]["dispatches"] = len(vals)
+    for v in kernels.values():
+        wc = v.get("SQ_WAVE_CYCLES") or 0.0
+        lds = v.get("SQ_ACTIVE_INST_LDS") or 0.0
+        v["wait_any_per_wave_cycle"] = v.get("SQ_WAIT_ANY", 0.0) / wc if wc else None
+        v["wait_inst_per_wave_cycle"] = v.get("SQ_WAIT_INST_ANY", 0.0) / wc if wc else None
+        v["lds_conflict_per_lds_active"] = v.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds if lds else None
+    data = {"source_hash": kernel_source_hash(), "counters": list(SQ_COUNTERS), "kernels": kernels}
+    Path(out_path).write_text(json.dumps(data, indent=1) + "\n")
+    return data
+
+
 def traffic_summary(fetch_csv, write_csv, out_path):
     """profiles/traffic.json from the two counter passes: per kernel, the median
     FETCH_SIZE and WRITE_SIZE per dispatch (KiB), each scaled by known bytes /
     counted bytes of the plain copy.  GEMV dispatches are attributed to batch
     sizes by launch order (traffic_run launches them in WORKLOADS[2].ms order)."""
-    import synth
-    ms = list(synth.WORKLOADS[2].ms)
-
-    def classify(name):
-        if "neg_kernel" in name:
-            return "calib_copy"
-        if "gemv_" in name and "_kernel" in name:
-            return "gemv"
-        if "quantize_kernel" in name:
-            return "quantize_fp32_5120x5120"
-        if "gemm_mfma_kernelILi256" in name or "gemm_mfma_kernel<256" in name:
-            return "gemm_2048x17408x5120"
-        return None
-
     def medians(path, counter):
-        by = {}
-        gemv = []
-        for did, name, cnt, val in _pmc_rows(path):
-            if cnt != counter:
-                continue
-            key = classify(name)
-            if key == "gemv":
-                gemv.append(val)
-            elif key:
-                by.setdefault(key, []).append(val)
-        if gemv:
-            per = len(gemv) // len(ms)
-            for i, m in enumerate(ms):
-                by[f"gemv_5120x5120_m{m}"] = gemv[i * per:(i + 1) * per]
+        by = _traffic_groups(path, counter)
         return {k: float(np.median(v)) for k, v in by.items()}, {k: len(v) for k, v in by.items()}
 
     fetch, nf = medians(fetch_csv, "FETCH_SIZE")
@@ -761,6 +799,8 @@ def main():
                     help="run the launches the MfmaUtil / MfmaFlopsF16 counter pass reads")
     ap.add_argument("--mfma-summary", metavar="PMC_CSV",
                     help="write profiles/mfma.json from that counter pass")
+    ap.add_argument("--sq-summary", metavar="PMC_CSV",
+                    help="write profiles/sq.json from an SQ counter pass over --traffic")
     ap.add_argument("--trace-summary", metavar="TRACE_CSV",
                     help="print per-batch-size GEMV durations from a kernel-trace CSV of a default run")
     args = ap.parse_args()
@@ -776,6 +816,9 @@ def main():
         return
     if args.mfma_summary:
         print(json.dumps(mfma_summary(args.mfma_summary, ROOT / "profiles" / "mfma.json"), indent=1))
+        return
+    if args.sq_summary:
+        print(json.dumps(sq_summary(args.sq_summary, ROOT / "profiles" / "sq.json"), indent=1))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
