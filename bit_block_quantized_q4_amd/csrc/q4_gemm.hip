@@ -16,7 +16,8 @@
 //     with 4 waves of 64 x 64), k steps of 64 (two Q4_0 blocks), two LDS
 //     stages.  Activations arrive by direct global->LDS copies
 //     (global_load_lds_dwordx4) into an XOR swizzle (piece c of row r at
-//     r*8 + (c ^ (r & 7))) so that operand reads hit distinct banks.  Each
+//     r*8 + (c ^ key(r)), key(r) = (r & 7) ^ ((r >> 3) & 1)) under which the
+//     16-byte operand reads have no bank conflicts.  Each
 //     thread owns weight units (one whole block of one row), loads them two
 //     steps ahead, dequantises them with byte permutes, the 1024+q / 64+q
 //     exponent trick, an exact packed subtraction and one packed multiply by
@@ -150,7 +151,13 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
 constexpr int kBK = 64;            // k per step: two Q4_0 blocks
 constexpr int kRowBytes16 = 128;   // one tile row of 64 fp16 = 8 pieces of 16 bytes
 
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+// Swizzle key of LDS row r (128-byte rows of eight 16-byte pieces): piece c
+// of row r sits at r * 8 + (c ^ key(r)).  Sixteen consecutive rows reading
+// one piece column land in sixteen distinct 16-byte bank groups of a 256-byte
+// bank window (rows r and r + 8 differ in the key's low bit), and any eight
+// consecutive rows in eight distinct groups of a 128-byte window.
+__device__ __forceinline__ int swz_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ swz_key(r)); }
 
 // One weight unit: one block of a row (scale and 16 code bytes) as the
 // 20-byte aligned window w0..w4 that contains it.
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
   for (int i = 0; i < A_COPIES; ++i) {
     const int P = NTH * i + tid;
     const int r = P >> 3;
-    const int c = (P & 7) ^ (r & 7);
+    const int c = (P & 7) ^ swz_key(r);
     const int64_t row = m0 + r < m ? m0 + r : m - 1;
     asrc[i] = x + row * k + 8 * c;
   }
@@ -493,7 +500,7 @@ __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
   for (int i = 0; i < 4; ++i) {
     const int P = 256 * i + tid;
     const int r = P >> 3;
-    const int c = (P & 7) ^ (r & 7);
+    const int c = (P & 7) ^ swz_key(r);
     const int64_t rr = m0 + r < m ? r : m - 1 - m0;
     aoff[i] = static_cast<uint32_t>((rr * k + 8 * c) * 2);
   }
@@ -553,7 +560,7 @@ __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
   // Fragment reads from a lane base plus compile-time offsets (stage, buffer,
   // step within the segment, fragment).  Reads past the last step are of
   // valid LDS addresses and unused.
-  const uint8_t* const abase = smem + lc * 128 + 16 * (apiece ^ (lc & 7));  // swz(32 i + lc, apiece)
+  const uint8_t* const abase = smem + swz(lc, apiece) * 16;  // + 32 i rows: swz(32 i + lc, apiece)
   const uint8_t* const wbase = smem + kSkWOff + lc * kSkSeg + 16 * b;
   auto read_a = [&](auto stage_c, half8_t (&fa)[4]) {
     constexpr int stage = decltype(stage_c)::value;
