@@ -215,14 +215,20 @@ def bench_quantize(q4, torch, dev, w_host, reps, rotate_bytes):
                          "traffic": load_traffic("quantize_fp32_5120x5120")}}
 
 
-def gemm_setup(q4, torch, dev, x_dtype=None):
+def gemm_setup(q4, torch, dev, x_dtype=None, dense=False):
+    """The prefill workload's launches.  With dense=True also returns
+    dense(cs): the same product in cs-row launches of the fp16 library GEMM
+    (torch.mm) on the unquantised weights rounded to fp16, a same-box
+    reference for the matrix-core kernels."""
     import synth
     wl = synth.WORKLOADS[4]
     lin = wl.linears[0]
     n, k, m = lin.n, lin.k, 2048
     w = synth.workload_weights(wl, lin)
-    packed = q4.q4_quantize(torch.from_numpy(w).to(dev))
-    del w
+    wd = torch.from_numpy(w).to(dev)
+    packed = q4.q4_quantize(wd)
+    wt = wd.half().t().contiguous() if dense else None  # [k, n] fp16, contiguous
+    del w, wd
     x = torch.from_numpy(synth.workload_activations(wl, k, m)).to(dev)
     if x_dtype is not None:
         x = x.to(x_dtype)
@@ -240,7 +246,16 @@ def gemm_setup(q4, torch, dev, x_dtype=None):
                 q4.q4_gemm(x[c * cs:(c + 1) * cs], packed, y=y[c * cs:(c + 1) * cs], workspace=work)
         return fn
 
-    return m, n, k, whole, chunked
+    if not dense:
+        return m, n, k, whole, chunked
+
+    def dense_chunked(cs):
+        def fn():
+            for c in range(m // cs):
+                torch.mm(x[c * cs:(c + 1) * cs], wt, out=y[c * cs:(c + 1) * cs])
+        return fn
+
+    return m, n, k, whole, chunked, dense_chunked
 
 
 def time_gemm_calls(torch, fn, reps):
@@ -261,7 +276,7 @@ def bench_gemm(q4, torch, dev, reps):
     smaller chunks bound the activation memory a step holds, at the cost of
     streaming the packed weight once per chunk and of fewer output tiles per
     launch."""
-    m, n, k, whole, chunked = gemm_setup(q4, torch, dev)
+    m, n, k, whole, chunked, dense = gemm_setup(q4, torch, dev, dense=True)
     flop = 2.0 * m * n * k
     res = {}
     for name, fn, calls in (("whole_2048", whole, 1), ("chunked_8x256", chunked(256), 8)):
@@ -269,6 +284,14 @@ def bench_gemm(q4, torch, dev, reps):
         tf = flop / avg_s / 1e12
         res[name] = {"mean_us": avg_s * 1e6, "launches": calls, "tflops": tf,
                      "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS}
+    # the fp16 library GEMM of the same shapes on the same box (context, not
+    # the metric): speed of the Q4_0 launches relative to it
+    lib = {}
+    for name, cs in (("whole_2048", m), ("chunked_8x256", 256)):
+        avg_s = time_gemm_calls(torch, dense(cs), reps)
+        lib[name] = {"mean_us": avg_s * 1e6, "frac_mfma": flop / avg_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                     "q4_speed_vs_library": avg_s * 1e6 / res[name]["mean_us"]}
+    res["dense_fp16_library"] = {"op": "torch.mm, fp16 x and fp16 weights [k, n] contiguous", **lib}
     sweep = []
     for cs in CHUNK_ROWS:
         avg_s = time_gemm_calls(torch, chunked(cs), reps)
