@@ -193,6 +193,36 @@ def bench_gemv(q4, torch, dev, steps, warmup, rotate_bytes):
     }
 
 
+def bench_gemv_dense_library(torch, dev, s, per_m, steps, rotate_bytes):
+    """Context, not the metric: the same decode products through the fp16
+    library GEMM (torch.mm) on the unquantised weights rounded to fp16, as a
+    contiguous [k, n] operand, rotated over >= rotate_bytes like the packed
+    copies; and the Q4_0 launches' speed relative to it."""
+    n, k, ms = s["n"], s["k"], s["ms"]
+    wt0 = torch.from_numpy(s["w_host"]).to(dev).half().t().contiguous()
+    dbytes = n * k * 2
+    copies = max(4, -(-rotate_bytes // dbytes))
+    wts = [wt0] + [wt0.clone() for _ in range(copies - 1)]
+    q4_us = {r["m"]: r["mean_us"] for r in per_m}
+    rows = []
+    for m in ms:
+        x, y = s["x"][:m], s["ys"][m]
+
+        def fn():
+            for i in range(steps):
+                torch.mm(x, wts[i % copies], out=y)
+        g = capture(torch, fn)
+        g.replay()
+        avg_s = replay_seconds(torch, g) / steps
+        del g
+        rows.append({"m": m, "mean_us": avg_s * 1e6, "weight_gbs": dbytes / avg_s / 1e9,
+                     "q4_speed_vs_library": avg_s * 1e6 / q4_us[m]})
+    del wts, wt0
+    torch.cuda.empty_cache()
+    return {"op": "torch.mm, fp16 x and fp16 weights [k, n] contiguous", "weight_bytes": dbytes,
+            "copies_rotated": copies, "per_m": rows}
+
+
 def bench_quantize(q4, torch, dev, w_host, reps, rotate_bytes):
     n, k = w_host.shape
     in_bytes = n * k * 4
@@ -882,6 +912,8 @@ def main():
                      "alg_bytes_per_launch": dom["alg_bytes"]},
         "per_m": g["per_m"],
     })
+    out["gemv_dense_fp16_library"] = bench_gemv_dense_library(
+        torch, dev, g["setup"], g["per_m"], args.steps, rotate)
     if args.only in ("all", "quantize"):
         out["quantize"] = bench_quantize(q4, torch, dev, g["w_host"], 20, rotate)
     if args.only in ("all", "gemm"):
