@@ -790,7 +790,10 @@ def trace_summary(trace_csv, steps, warmup):
     with open(trace_csv) as f:
         for r in csv.DictReader(f):
             name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
-            if "gemv_" in name and "_kernel" in name:
+            # this library's kernels (demangled when launched directly, mangled
+            # when replayed from a graph)
+            ours = "q4::" in name or name.startswith("_ZN2q4")
+            if ours and "gemv_" in name and "_kernel" in name:
                 start = int(r.get("Start_Timestamp") or r.get("Start-Timestamp"))
                 end = int(r.get("End_Timestamp") or r.get("End-Timestamp"))
                 rows.append((start, end - start, name))
