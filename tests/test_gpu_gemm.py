@@ -103,6 +103,25 @@ def test_layer_workload_sampled(q4lib, gpu):
                                 what=f"layer/{lin.name} m{m}")
 
 
+def test_long_ragged_prefill_sampled(q4lib, gpu):
+    """8191 prompt rows (the last 256-row tile one row short) on the 5120 x 5120
+    projection, fp16 output: sampled rows, the first and last of every
+    row-tile boundary among them, against the oracle."""
+    import torch
+    wl = synth.WORKLOADS[2]
+    lin = wl.linears[0]
+    w = workload_weights_cached(wl, lin)
+    packed_d = q4lib.q4_quantize(to_dev(w, gpu))
+    packed = to_host(packed_d)
+    del w
+    m = 8191
+    x = synth.random_activations(81, m, lin.k, "f16")
+    y = to_host(q4lib.q4_gemm(to_dev(x, gpu), packed_d, y_dtype=torch.float16))
+    assert np.isfinite(y).all()
+    rows = np.unique(np.concatenate([sample_rows(m, 8, 7), [0, 255, 256, 4095, 4096, 7935, 7936, m - 1]]))
+    assert_matmul_close(y[rows], x[rows], packed, lin.n, lin.k, what=f"{wl.name} m{m}")
+
+
 def test_deterministic(q4lib, gpu):
     import torch
     n, k = 3000, 5120
