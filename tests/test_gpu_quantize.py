@@ -115,3 +115,27 @@ def test_bf16_edge_case_weights(q4lib, gpu):
     wb = synth.bf16_bits(synth.edge_case_weights(7, n, k))
     got = to_host(q4lib.q4_quantize(to_dev_bf16(wb, gpu)))
     assert np.array_equal(got, oracle.quantize(oracle.widen_bf16(wb)))
+
+
+def test_more_than_2_31_elements(q4lib, gpu):
+    """A 65537 x 32768 fp32 weight (2^31 + 32768 elements, 8.6 GB): element and
+    byte offsets pass 2^31 and 2^32.  Rows on both sides of element 2^31 (row
+    65536 starts there) and spread over the weight match the oracle byte for
+    byte.  The weight is drawn on the device; only sampled rows come back."""
+    import torch
+    n, k = 65537, 32768
+    g = torch.Generator(device=gpu)
+    g.manual_seed(2 ** 31 + 1)
+    w = torch.randn((n, k), device=gpu, generator=g)
+    w[-1, :64] = torch.tensor([0.0] * 32 + [-1e-30] * 31 + [3.0], device=gpu)  # odd blocks at the end
+    packed = q4lib.q4_quantize(w)
+    rows = np.unique(np.concatenate([np.random.default_rng(231).choice(n, 12, replace=False),
+                                     [0, 32767, 32768, 65534, 65535, 65536]]))
+    rows_t = torch.from_numpy(rows).to(gpu)
+    w_rows = w.index_select(0, rows_t).cpu().numpy()
+    p_rows = packed.index_select(0, rows_t).cpu().numpy()
+    del w, packed
+    torch.cuda.empty_cache()
+    want = oracle.quantize(w_rows)
+    assert np.array_equal(p_rows, want), [int(r) for r, a, b in zip(rows, p_rows, want)
+                                          if not np.array_equal(a, b)]
