@@ -313,3 +313,27 @@ def test_balanced_long_k(q4lib, gpu, m, n, k):
     g = run_gemv(q4lib, x, packed, n, k, "f32", gpu)
     cols = np.unique(np.concatenate([np.arange(0, n, 11), [n - 1]]))
     assert_matmul_close(g[:, cols], x, packed, n, k, cols=cols, what=f"m{m} n{n} k{k}")
+
+
+def test_packed_weight_past_2_gib(q4lib, gpu):
+    """A 131072 x 32768 weight: 2.4 GB of packed rows (byte offsets past 2^31),
+    quantised on the device from 17 GB of fp32.  Sampled output features, the
+    first and last rows among them, match the oracle on their own packed rows
+    at m = 1 and 16."""
+    import torch
+    n, k = 131072, 32768
+    g = torch.Generator(device=gpu)
+    g.manual_seed(131072)
+    w = torch.randn((n, k), device=gpu, generator=g)
+    w.mul_(0.02)
+    packed_d = q4lib.q4_quantize(w)
+    del w
+    torch.cuda.empty_cache()
+    cols = np.unique(np.concatenate([np.random.default_rng(2).choice(n, 30, replace=False),
+                                     [0, 65535, 65536, 119304, n - 1]]))
+    packed_cols = to_host(packed_d.index_select(0, torch.from_numpy(cols).to(gpu)))
+    for m in (1, 16):
+        x = synth.random_activations(m + 131, m, k, "f16")
+        y = to_host(q4lib.q4_gemv(to_dev(x, gpu), packed_d, y_dtype=torch.float32))
+        assert np.isfinite(y).all()
+        assert_matmul_close(y[:, cols], x, packed_cols, len(cols), k, what=f"{n}x{k} m{m}")
