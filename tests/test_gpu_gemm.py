@@ -122,6 +122,23 @@ def test_long_ragged_prefill_sampled(q4lib, gpu):
     assert_matmul_close(y[rows], x[rows], packed, lin.n, lin.k, what=f"{wl.name} m{m}")
 
 
+@pytest.mark.parametrize("m", [300, 1100])
+def test_long_k_sampled(q4lib, gpu, m):
+    """k = 65536 (2048 Q4_0 blocks per row) on the slice-K tile (m = 300) and
+    the 256 x 256 tile (m = 1100), ragged n: sampled rows against the oracle."""
+    import torch
+    n, k = 700, 65536
+    w = synth.random_weights(65, n, k, "normal")
+    packed_d = q4lib.q4_quantize(to_dev(w, gpu))
+    packed = to_host(packed_d)
+    del w
+    x = synth.random_activations(m + 65, m, k, "f16")
+    y = to_host(q4lib.q4_gemm(to_dev(x, gpu), packed_d, y_dtype=torch.float32))
+    assert np.isfinite(y).all()
+    rows = sample_rows(m, 8, m)
+    assert_matmul_close(y[rows], x[rows], packed, n, k, what=f"{m}x{n}x{k}")
+
+
 def test_deterministic(q4lib, gpu):
     import torch
     n, k = 3000, 5120
