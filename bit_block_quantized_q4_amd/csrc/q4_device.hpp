@@ -48,26 +48,6 @@ __device__ __forceinline__ half8_t unpack8(uint32_t w0, uint32_t w1, const Unpac
   return __builtin_bit_cast(half8_t, r);
 }
 
-// The eight codes of unpack8 as fp16 subnormals q * 2^-24 (exact: the nibble
-// is the whole mantissa of a zero exponent field), same operand order.  Low
-// nibbles are masked in place; high nibbles are shifted down within each
-// 16-bit half.  The matrix product of these with x is 2^-24 * sum(x * q): the
-// caller adds the -8 * 2^-24 * sum(x) offset and rescales by 2^24.
-template <int O>
-__device__ __forceinline__ half8_t unpack8_sub(uint32_t w0, uint32_t w1) {
-  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-  constexpr uint32_t sel01 = (O + 0) | (0x0cu << 8) | ((O + 1u) << 16) | (0x0cu << 24);
-  constexpr uint32_t sel23 = (O + 2) | (0x0cu << 8) | ((O + 3u) << 16) | (0x0cu << 24);
-  const uint32_t t01 = __builtin_amdgcn_perm(w1, w0, sel01);  // [c0, 0, c1, 0]
-  const uint32_t t23 = __builtin_amdgcn_perm(w1, w0, sel23);  // [c2, 0, c3, 0]
-  u32x4 r;
-  r[0] = t01 & 0x000F000Fu;
-  r[1] = t23 & 0x000F000Fu;
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, t01) >> u16x2{4, 4});
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, t23) >> u16x2{4, 4});
-  return __builtin_bit_cast(half8_t, r);
-}
-
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 // 16-byte global -> LDS copy for every active lane: lane l's bytes land at

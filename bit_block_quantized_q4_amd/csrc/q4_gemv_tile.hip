@@ -1,6 +1,8 @@
 // Q4_0 decode GEMV on 16 x 16 x 32 matrix cores: y[i, r] = sum_j x[i, j] w[r, j]
-// for a batch of up to 32 activation rows (llama.cpp's Q4_0 block page, block
-// layout; the serving page's batched decode step).
+// for a batch of up to 32 activation rows (the batched decode stage of
+// "Vertical disaggregation: maximizing throughput on heterogeneous silicon",
+// section "Every cycle counts: custom kernels", over its one shared Q4_0
+// weight format).
 //
 // One workgroup owns R <= 16 T consecutive weight rows over the whole of K,
 // so no partial sums leave the workgroup.  When R is not a multiple of 16
@@ -13,14 +15,17 @@
 // in flight while eight computing waves work on phase p.  Within a phase
 // wave w owns blocks w PB / 8 .. (w + 1) PB / 8 - 1 for all 16 T rows;
 // each (row tile, block) pair is one v_mfma_f32_16x16x32_f16 with 16
-// activation rows on the A side and 16 weight rows on the B side.  The block's
-// 32 codes enter as fp16 subnormals q 2^-24 (the nibble is the whole
-// mantissa), and the matrix core's accumulator input carries the code offset,
-// -8 2^-24 sum(x), which one extra product of the activations with a
-// constant gives once per block for all row tiles; the block scale d is then
-// applied in fp32 to the 4 outputs the lane holds (lane l: weight row l % 16,
-// activation rows 4 (l / 16) .. +3) and the sums are rescaled by 2^24 at the
-// end.
+// activation rows on the A side and 16 weight rows on the B side.  The
+// block's 32 codes enter as exact fp16 integers q - 8 (the 1024 + q / 64 + q
+// exponent trick and one exact packed subtraction), so every product x (q - 8)
+// is exact and the block sum's rounding error is relative to
+// sum |x (q - 8)|; the block scale d is then applied in fp32 to the 4
+// outputs the lane holds (lane l: weight row l % 16, activation rows
+// 4 (l / 16) .. +3).  (An earlier form fed the codes as fp16 subnormals
+// q 2^-24 and carried -8 2^-24 sum(x) through a separately rounded
+// accumulator input; its error then scaled with sum |x| instead of
+// sum |x w| and could exceed the tolerance on blocks where large activations
+// meet zero weights.)
 //
 // Bank layout: a weight row occupies an odd number of 16-byte pieces (the
 // phase's 9 PB / 8 data pieces plus one padding piece), so the 16 rows one
@@ -194,6 +199,7 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
         xa[j][h][t] = G::wbytes + ar * (G::xp * 16) + 16 * (pc ^ sw) + 8 * (g & 1);
       }
   }
+  const UnpackConsts kc = make_unpack_consts();
   float4_t acc[T][AT];
 #pragma unroll
   for (int i = 0; i < T; ++i)
@@ -216,19 +222,6 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
         }
         A[j][t] = __builtin_bit_cast(half8_t, a);
       }
-    // Code offset of block j: -8 2^-24 sum over the block of x, per activation
-    // row, in the output layout (a product with a constant -2^-21 operand).
-    const half8_t kneg = {static_cast<half_t>(-0x1p-21f), static_cast<half_t>(-0x1p-21f),
-                          static_cast<half_t>(-0x1p-21f), static_cast<half_t>(-0x1p-21f),
-                          static_cast<half_t>(-0x1p-21f), static_cast<half_t>(-0x1p-21f),
-                          static_cast<half_t>(-0x1p-21f), static_cast<half_t>(-0x1p-21f)};
-    float4_t C[G::jb][AT];
-#pragma unroll
-    for (int j = 0; j < G::jb; ++j)
-#pragma unroll
-      for (int t = 0; t < AT; ++t)
-        C[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j][t], kneg, float4_t{0.f, 0.f, 0.f, 0.f},
-                                                         0, 0, 0);
     unroll<0, T>([&](auto ii) {
       constexpr int i = decltype(ii)::value;
       constexpr int rt = i * 16 * G::wstride;
@@ -248,15 +241,16 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
           // even block: code bytes 4g .. 4g+3 are bytes 2..5 of the window at 4g
           const uint32_t w0 = *reinterpret_cast<const uint32_t*>(slot + rg0 + bo);
           const uint32_t w1 = *reinterpret_cast<const uint32_t*>(slot + rg0 + bo + 4);
-          bw = unpack8_sub<2>(w0, w1);
+          bw = unpack8<2>(w0, w1, kc);
         } else {
           // odd block: they are the aligned dword at 4g + 2
           const uint32_t c = *reinterpret_cast<const uint32_t*>(slot + rg0 + bo + 2);
-          bw = unpack8_sub<0>(c, c);
+          bw = unpack8<0>(c, c, kc);
         }
 #pragma unroll
         for (int t = 0; t < AT; ++t) {
-          const float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j][t], bw, C[j][t], 0, 0, 0);
+          const float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              A[j][t], bw, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[i][t][e] = d * D[e] + acc[i][t][e];
         }
@@ -323,7 +317,6 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) sum += q[w * kWave * 4];
-    sum *= 0x1p24f;  // exact rescale of the subnormal code products
     const int64_t row = row0 + 16 * i + wr;
     if (16 * i + wr < rv) {
       const int64_t off = static_cast<int64_t>(ar) * n + row;

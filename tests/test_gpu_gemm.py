@@ -64,13 +64,15 @@ def test_edge_case_weights(q4lib, gpu):
 
 
 def test_prefill_chunked_and_whole(q4lib, gpu):
-    """2048 prompt rows as one batch and as 8 chunks of 256 (pointer offsets)."""
+    """2048 prompt rows as one batch and as 8 chunks of 256 (pointer offsets):
+    every one of the 2048 x 17408 outputs of both runs against the oracle."""
     import torch
     wl = synth.WORKLOADS[4]
     lin = wl.linears[0]
     w = workload_weights_cached(wl, lin)
     packed_d = q4lib.q4_quantize(to_dev(w, gpu))
     packed = to_host(packed_d)
+    assert np.array_equal(packed[:16], oracle.quantize(w[:16]))
     del w
     x = synth.workload_activations(wl, lin.k, 2048)
     xd = to_dev(x, gpu)
@@ -78,16 +80,18 @@ def test_prefill_chunked_and_whole(q4lib, gpu):
     chunked = torch.empty_like(whole)
     for c in range(8):
         q4lib.q4_gemm(xd[c * 256:(c + 1) * 256], packed_d, y=chunked[c * 256:(c + 1) * 256])
-    rows = np.unique(np.concatenate([sample_rows(2048, 40, 1), [255, 256, 1023, 1024, 1792]]))
+    y_ref, S = oracle.matmul_ref(x, packed, lin.n, lin.k)
     for name, y in (("whole", whole), ("chunked", chunked)):
-        assert_matmul_close(to_host(y)[rows], x[rows], packed, lin.n, lin.k,
-                            what=f"{wl.name}/{name}")
+        ok, worst, idx = oracle.check(to_host(y), y_ref, S)
+        assert ok, f"{wl.name}/{name}: worst |gpu-oracle|/bound = {worst:.3g} at {idx}"
     again = q4lib.q4_gemm(xd, packed_d, y_dtype=torch.float16)
     assert torch.equal(again.view(torch.int16), whole.view(torch.int16))
 
 
-def test_layer_workload_sampled(q4lib, gpu):
-    """All seven Student-t linears at M = 256 and 4096, sampled rows x all features."""
+def test_layer_workload(q4lib, gpu):
+    """All seven Student-t linears of the layer: at M = 256 every output; at
+    M = 4096 a seeded set of at least 512 full rows per linear (over 12.5 % of
+    the rows, both sides of every 256-row tile boundary among them) against the oracle."""
     import torch
     wl = synth.WORKLOADS[5]
     for lin in wl.linears:
@@ -98,7 +102,12 @@ def test_layer_workload_sampled(q4lib, gpu):
         for m in (256, 4096):
             x = synth.workload_activations(wl, lin.k, m)
             y = to_host(q4lib.q4_gemm(to_dev(x, gpu), packed_d, y_dtype=torch.float16))
-            rows = sample_rows(m, 12, m + lin.tensor_id)
+            if m == 256:
+                rows = np.arange(m)
+            else:
+                rows = np.unique(np.concatenate([sample_rows(m, 512, m + lin.tensor_id),
+                                                 np.arange(255, m, 256), np.arange(0, m, 256)]))
+                assert len(rows) >= 512
             assert_matmul_close(y[rows], x[rows], packed, lin.n, lin.k,
                                 what=f"layer/{lin.name} m{m}")
 
@@ -253,3 +262,43 @@ def test_bf16_chunked_matches_oracle(q4lib, gpu):
     rows = sample_rows(m, 64, 5)
     assert_matmul_close(to_host(y)[rows], oracle.widen_bf16(xb)[rows], to_host(packed_d), n, k,
                         what="bf16 chunks")
+
+
+def wide_range_f16(seed, m, k):
+    """fp16 activations whose magnitudes span the whole fp16 range, subnormals
+    2^-24 .. 2^-15 and exact zeros included, with random signs."""
+    rng = np.random.default_rng(seed)
+    e = rng.uniform(-24.0, 15.99, size=(m, k))
+    x = np.exp2(e).astype(np.float32)
+    x = np.where(rng.random((m, k)) < 0.5, -x, x).astype(np.float16)
+    x[rng.random((m, k)) < 0.02] = 0
+    return x
+
+
+def edge_rows(seed, n, k, top):
+    """n rows of quantiser corner-case blocks: 96 generated rows repeated (the
+    block patterns cycle along each row, so repeats stay varied)."""
+    base = synth.edge_case_weights(seed, 96, k, top=top)
+    reps = (n + 95) // 96
+    return np.ascontiguousarray(np.tile(base, (reps, 1))[:n])
+
+
+# (m, n, k): slice-K tiles (m < 1024, k % 256 == 0, k >= 1024), with and
+# without a split-K tail; 256 x 256 tiles with a split-K tail (m >= 1024).
+EDGE_GEMM = [(256, 4100, 1536), (700, 6000, 5120), (1100, 4100, 1536), (2048, 8448, 5120)]
+
+
+@pytest.mark.parametrize("m,n,k", EDGE_GEMM)
+def test_edge_case_weights_main_kernels(q4lib, gpu, m, n, k):
+    """The quantiser's corner-case blocks (those whose dequantised weights fit
+    fp16) through the slice-K, 256 x 256 and split-K tail kernels, with N(0, 1)
+    and with wide-range fp16 activations; every output checked."""
+    w = edge_rows(131 + k, n, k, 65504.0)
+    packed = oracle.quantize(w)
+    del w
+    pd = to_dev(packed, gpu)
+    for name, x in (("normal", synth.random_activations(137 + m, m, k, "f16")),
+                    ("wide", wide_range_f16(139 + m + k, m, k))):
+        import torch
+        g = to_host(q4lib.q4_gemm(to_dev(x, gpu), pd, y_dtype=torch.float32, n=n, k=k))
+        assert_matmul_close(g, x, packed, n, k, what=f"edge {name} m{m} n{n} k{k}")

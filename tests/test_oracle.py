@@ -297,6 +297,53 @@ def test_exact_rational_dot_products(xdt):
             assert abs(Fr(float(S[mi, ni])) - sacc) <= Fr(1, 10 ** 12) * max(sacc, Fr(1))
 
 
+def test_cols_subset_equals_full_columns():
+    """matmul_ref(..., cols=c) returns the full product's columns c, in the
+    order given (unsorted and repeated indices included), for y and S."""
+    m, n, k = 4, 37, 96
+    w = synth.random_weights(14, n, k, "student_t")
+    x = synth.random_activations(15, m, k, "f16")
+    packed = oracle.quantize(w)
+    y, S = oracle.matmul_ref(x, packed, n, k)
+    for cols in ([0], [n - 1, 0, 5], [3, 3, 36, 17], list(range(n))):
+        yc, Sc = oracle.matmul_ref(x, packed, n, k, cols=cols)
+        assert yc.shape == (m, len(cols))
+        assert np.array_equal(yc, y[:, cols]) and np.array_equal(Sc, S[:, cols])
+
+
+def test_cancellation_case_closed_form():
+    """Blocks with one weight +-1.0 (code 0, d = -+0.125) and 31 zeros (code 8):
+    y is the sum of the activations at the nonzero weights, signed, exactly
+    (every value is dyadic), and S the sum of their magnitudes."""
+    n, k = 8, 128
+    w = np.zeros((n, k), np.float32)
+    for r in range(n):
+        w[r, (r % 4)::32] = 1.0 if (r // 4) % 2 == 0 else -1.0
+    x = np.full((2, k), 1024.0, np.float32)
+    x[:, 0::32] = np.float32(2.0 ** -10)
+    x[1, 1::32] = np.float32(-3 * 2.0 ** -10)
+    packed = oracle.quantize(w)
+    d, q = oracle.unpack(packed, n, k)
+    assert set(np.unique(q)) == {0, 8}
+    assert set(np.abs(d.astype(np.float32)).ravel()) == {0.125}
+    y, S = oracle.matmul_ref(x.astype(np.float16), packed, n, k)
+    for r in range(n):
+        sgn = 1.0 if (r // 4) % 2 == 0 else -1.0
+        for i in range(2):
+            col = x[i, (r % 4)::32].astype(np.float64)
+            assert y[i, r] == sgn * col.sum()
+            assert S[i, r] == np.abs(col).sum()
+
+
+def test_packed_size_matches_quantized_bytes():
+    """n rows of k / 32 blocks of 18 bytes: the byte count quantize produces."""
+    for n, k in ((1, 32), (3, 64), (17, 96), (5, 512)):
+        w = synth.random_weights(16, n, k)
+        assert oracle.packed_size(n, k) == oracle.quantize(w).nbytes == n * (k // 32) * 18
+    with pytest.raises(ValueError):
+        oracle.packed_size(4, 48)
+
+
 # ---------------------------------------------------------------- bf16 inputs
 
 def _bf16_by_fields(bits: int) -> float:
