@@ -9,7 +9,7 @@ with ``python -m bit_block_quantized_q4_amd.build``).
 
 Functions mirror the C entry points: ``q4_packed_size``,
 ``q4_gemm_workspace_size``, ``q4_gemm_workspace_size_dt``, ``q4_quantize``, ``q4_gemv``, ``q4_gemm``,
-``q4_status_string``, ``q4_abi_version``.
+``q4_gemm_noalloc``, ``q4_status_string``, ``q4_abi_version``.
 """
 
 from __future__ import annotations
@@ -34,6 +34,9 @@ Q4_ERR_DTYPE = 3
 Q4_ERR_ALIGNMENT = 4
 Q4_ERR_HIP = 5
 Q4_ERR_WORKSPACE = 6
+Q4_ERR_UNSUPPORTED = 7
+Q4_ERR_SCRATCH = 8
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 Q4_F32 = 0
 Q4_F16 = 1
@@ -55,6 +58,9 @@ _SIGS = {
                                ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                ctypes.c_size_t, ctypes.c_void_p]),
+    "q4_gemm_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
 }
 
 
@@ -250,4 +256,19 @@ def q4_gemm(x, packed, y=None, y_dtype=None, workspace=None, stream=None, n=None
     _check(lib().q4_gemm(x.data_ptr(), _dtype_code(x), packed.data_ptr(), y.data_ptr(),
                          _dtype_code(y), m, n, k, wptr, wbytes,
                          _stream_handle(stream, x.device)), "q4_gemm")
+    return y
+
+
+def q4_gemm_noalloc(x, packed, y, stream=None, n=None, k=None):
+    """q4_gemm with its workspace taken from the library's fixed per-device
+    scratch array (no allocation by the library; y must be given).  Calls that
+    may overlap on one device race on that array."""
+    _need_device(x, "x")
+    _need_device(packed, "packed")
+    _need_device(y, "y")
+    n, k = packed_shape(packed, n, k)
+    m = int(x.numel() // k) if x.dim() != 2 else int(x.shape[0])
+    _check(lib().q4_gemm_noalloc(x.data_ptr(), _dtype_code(x), packed.data_ptr(), y.data_ptr(),
+                                 _dtype_code(y), m, n, k, _stream_handle(stream, x.device)),
+           "q4_gemm_noalloc")
     return y

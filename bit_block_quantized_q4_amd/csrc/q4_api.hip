@@ -1,8 +1,16 @@
 // libq4 C ABI: argument validation and dispatch.  Every check runs on the host
 // before anything touches the device; the library keeps no state, never
 // allocates, frees or synchronises.
+#include <mutex>
+
 #include "q4.h"
 #include "q4_internal.hpp"
+
+// Workspace of q4_gemm_noalloc: one copy per device that loads the library,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address is looked up per
+// device with hipGetSymbolAddress and only that address reaches a kernel.
+static __device__ __align__(256) uint8_t scratch[Q4_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -30,6 +38,26 @@ bool valid_nk(int64_t n, int64_t k) {
 }
 
 q4_status from_hip(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_HIP; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each device holds its own copy at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+q4_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q4_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return Q4_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return Q4_OK;
+}
 
 q4_status check_matmul(const void* x, int x_dtype, const void* packed, void* y,
                        int y_dtype, int64_t m, int64_t n, int64_t k) {
@@ -62,6 +90,7 @@ const char* q4_status_string(int status) {
     case Q4_ERR_HIP: return "HIP runtime refused the kernel launch";
     case Q4_ERR_WORKSPACE: return "workspace missing or too small";
     case Q4_ERR_UNSUPPORTED: return "the host CPU lacks AVX2, FMA or F16C";
+    case Q4_ERR_SCRATCH: return "the call needs more scratch than q4_gemm_noalloc's fixed array holds";
     default: return "unknown q4 status";
   }
 }
@@ -126,6 +155,24 @@ q4_status q4_gemm(const void* x, int x_dtype, const void* packed, void* y, int y
                                   static_cast<const uint8_t*>(packed),
                                   y, static_cast<q4::DType>(y_dtype), m, n, k,
                                   need > 0 ? workspace : nullptr,
+                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+q4_status q4_gemm_noalloc(const void* x, int x_dtype, const void* packed, void* y,
+                          int y_dtype, int64_t m, int64_t n, int64_t k, q4_stream_t stream) {
+  const q4_status st = check_matmul(x, x_dtype, packed, y, y_dtype, m, n, k);
+  if (st != Q4_OK) return st;
+  if (x_dtype != Q4_F16 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+  const size_t need = q4::gemm_workspace_bytes(m, n, k, static_cast<q4::DType>(x_dtype));
+  if (need > Q4_NOALLOC_SCRATCH_BYTES) return Q4_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    const q4_status sa = scratch_address(&ws);
+    if (sa != Q4_OK) return sa;
+  }
+  return from_hip(q4::launch_gemm(x, static_cast<q4::DType>(x_dtype),
+                                  static_cast<const uint8_t*>(packed),
+                                  y, static_cast<q4::DType>(y_dtype), m, n, k, ws,
                                   reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -77,8 +77,10 @@ typedef enum q4_status {
   Q4_ERR_ALIGNMENT = 4,   /* a pointer is not 16-byte aligned */
   Q4_ERR_HIP = 5,         /* the HIP runtime refused a launch */
   Q4_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
-  Q4_ERR_UNSUPPORTED = 7  /* the host CPU lacks an instruction set the call needs
+  Q4_ERR_UNSUPPORTED = 7, /* the host CPU lacks an instruction set the call needs
                              (q4_host.h) */
+  Q4_ERR_SCRATCH = 8      /* the call needs more scratch than q4_gemm_noalloc's
+                             fixed per-device array holds */
 } q4_status;
 
 typedef enum q4_dtype {
@@ -150,6 +152,26 @@ q4_status q4_gemm(const void *x, int x_dtype, const void *packed, void *y,
                   int y_dtype, int64_t m, int64_t n, int64_t k,
                   void *workspace, size_t workspace_bytes,
                   q4_stream_t stream);
+
+/* Bytes of the fixed per-device scratch array behind q4_gemm_noalloc. */
+#define Q4_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* q4_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation, kernels and results as q4_gemm, with the workspace taken
+ * from a fixed array of Q4_NOALLOC_SCRATCH_BYTES bytes that the library holds
+ * on each device it runs on until the process ends.  The array is the current
+ * device's (the device of `stream`); the first call on a device looks up its
+ * address once.  Calls whose workspace need, q4_gemm_workspace_size_dt(m, n,
+ * k, x_dtype), exceeds the array return Q4_ERR_SCRATCH before launching
+ * anything.  The call itself allocates nothing.  Every call on one device
+ * shares that device's array: calls that may overlap on one device (several
+ * streams, several host threads) race on it and must be serialised by the
+ * caller; its contents after a call are unspecified, and each call writes
+ * every scratch byte it reads.  Arguments, errors and layouts are q4_gemm's. */
+q4_status q4_gemm_noalloc(const void *x, int x_dtype, const void *packed, void *y,
+                          int y_dtype, int64_t m, int64_t n, int64_t k,
+                          q4_stream_t stream);
 
 #ifdef __cplusplus
 }

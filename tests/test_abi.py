@@ -10,7 +10,7 @@ import pytest
 ROOT = Path(__file__).resolve().parent.parent
 HEADER = ROOT / "include" / "q4.h"
 
-OK, INVALID, SHAPE, DTYPE, ALIGN, HIP, WORKSPACE = range(7)
+OK, INVALID, SHAPE, DTYPE, ALIGN, HIP, WORKSPACE, UNSUPPORTED, SCRATCH = range(9)
 F32, F16, BF16 = 0, 1, 2
 A = 0x10000          # stand-in, 16-byte aligned "device" addresses: never dereferenced
 B = 0x20000000
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(q4lib):
 
 def test_version_and_status_strings(q4lib):
     assert q4lib.q4_abi_version() == 1
-    for code in range(8):
+    for code in range(9):
         s = q4lib.q4_status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in q4lib.q4_status_string(99)
@@ -108,6 +108,23 @@ def test_gemm_argument_checks(q4lib):
     assert f(A, BF16, B, C, F16, 64, 8, 32, 0x60000008, needb, None) == ALIGN
     assert f(A, BF16, B, C, F16, 64, 8, 32, A, needb, None) == INVALID    # workspace over x
     assert f(A, BF16, B, C, BF16, 64, 8, 32, 0x60000000, needb, None) == DTYPE
+
+
+def test_gemm_noalloc_argument_checks(q4lib):
+    """q4_gemm_noalloc validates like q4_gemm and refuses, before any launch,
+    calls whose workspace need exceeds its fixed scratch array."""
+    f = q4lib.lib().q4_gemm_noalloc
+    assert f(None, F16, B, C, F16, 64, 8, 32, None) == INVALID
+    assert f(A, F32, B, C, F16, 64, 8, 32, None) == DTYPE
+    assert f(A, F16, B, C, F16, 0, 8, 32, None) == SHAPE
+    assert f(A + 8, F16, B, C, F16, 64, 8, 32, None) == ALIGN
+    assert f(A, F16, B, A, F16, 64, 8, 32, None) == INVALID
+    limit = q4lib.NOALLOC_SCRATCH_BYTES
+    m, k = 8192, 8192          # bf16 staging alone is m * k * 2 = 128 MiB
+    assert q4lib.q4_gemm_workspace_size_dt(m, 64, k, BF16) > limit
+    assert f(0x100000000, BF16, 0x800000000, 0xC00000000, F16, m, 64, k, None) == SCRATCH
+    header = HEADER.read_text()
+    assert f"#define Q4_NOALLOC_SCRATCH_BYTES ({limit >> 20}u << 20)" in header
 
 
 def test_binding_fails_loudly_without_library(q4lib, monkeypatch, tmp_path):
