@@ -16,6 +16,10 @@ namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 constexpr int64_t kMaxRows = int64_t(1) << 31;
+// Largest k of a matmul: the kernels address a tile's rows of x and of the
+// packed weight with 32-bit per-lane byte offsets (up to 128 rows of 2 k
+// bytes of activations), which stay below 2^32 for k <= 2^24.
+constexpr int64_t kMaxMatmulK = int64_t(1) << 24;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -62,7 +66,7 @@ q4_status scratch_address(void** out) {
 q4_status check_matmul(const void* x, int x_dtype, const void* packed, void* y,
                        int y_dtype, int64_t m, int64_t n, int64_t k) {
   if (!x || !packed || !y) return Q4_ERR_INVALID_ARG;
-  if (!valid_nk(n, k) || m < 1 || m >= kMaxRows || m > kMaxElems / k ||
+  if (!valid_nk(n, k) || k > kMaxMatmulK || m < 1 || m >= kMaxRows || m > kMaxElems / k ||
       m > kMaxElems / n)
     return Q4_ERR_SHAPE;
   if (!valid_in_dtype(x_dtype) || !valid_out_dtype(y_dtype)) return Q4_ERR_DTYPE;
@@ -130,8 +134,9 @@ size_t q4_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
 }
 
 size_t q4_gemm_workspace_size_dt(int64_t m, int64_t n, int64_t k, int x_dtype) {
-  if (!valid_nk(n, k) || m < 1 || m >= kMaxRows || m > kMaxElems / k) return 0;
-  if (x_dtype != Q4_F16 && x_dtype != Q4_BF16) return 0;
+  if (!valid_nk(n, k) || k > kMaxMatmulK || m < 1 || m >= kMaxRows || m > kMaxElems / k)
+    return 0;
+  if (!valid_in_dtype(x_dtype)) return 0;
   return q4::gemm_workspace_bytes(m, n, k, static_cast<q4::DType>(x_dtype));
 }
 
@@ -140,12 +145,11 @@ q4_status q4_gemm(const void* x, int x_dtype, const void* packed, void* y, int y
                   size_t workspace_bytes, q4_stream_t stream) {
   const q4_status st = check_matmul(x, x_dtype, packed, y, y_dtype, m, n, k);
   if (st != Q4_OK) return st;
-  if (x_dtype != Q4_F16 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
   const size_t need = q4::gemm_workspace_bytes(m, n, k, static_cast<q4::DType>(x_dtype));
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return Q4_ERR_WORKSPACE;
     if (!aligned16(workspace)) return Q4_ERR_ALIGNMENT;
-    const size_t xbytes = static_cast<size_t>(m) * k * 2;
+    const size_t xbytes = static_cast<size_t>(m) * k * dtype_bytes(x_dtype);
     if (overlap(workspace, need, x, xbytes) || overlap(workspace, need, y,
                 static_cast<size_t>(m) * n * dtype_bytes(y_dtype)) ||
         overlap(workspace, need, packed, q4_packed_size(n, k)))
@@ -162,7 +166,6 @@ q4_status q4_gemm_noalloc(const void* x, int x_dtype, const void* packed, void* 
                           int y_dtype, int64_t m, int64_t n, int64_t k, q4_stream_t stream) {
   const q4_status st = check_matmul(x, x_dtype, packed, y, y_dtype, m, n, k);
   if (st != Q4_OK) return st;
-  if (x_dtype != Q4_F16 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
   const size_t need = q4::gemm_workspace_bytes(m, n, k, static_cast<q4::DType>(x_dtype));
   if (need > Q4_NOALLOC_SCRATCH_BYTES) return Q4_ERR_SCRATCH;
   void* ws = nullptr;

@@ -164,5 +164,67 @@ __device__ __forceinline__ void tie_after(T& v) {
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
+// Whether any thread of the workgroup passed `flag`, through one word of the
+// kernel's own LDS (`word`, free at this point: no thread reads or writes it
+// after the first barrier until it returns).  Every thread must call it.  The
+// barriers also order the global stores made before it ahead of later
+// stores to the same outputs.  (__syncthreads_or would add static LDS, which
+// kernels that take all 160 KB as dynamic LDS cannot launch with.)
+__device__ __forceinline__ bool workgroup_any_flag(bool flag, uint32_t* word) {
+  __syncthreads();
+  if (threadIdx.x == 0) *word = 0u;
+  __syncthreads();
+  if (flag) *word = 1u;  // every writer writes the same value
+  __syncthreads();
+  return *word != 0u;
+}
+
+// Rows row0 .. row0 + nrows - 1 of y = x . dequant(W)^T for bf16 activations
+// on the exact route: x widened exactly to fp32, (q - 8) and d applied in
+// fp32 per block, fp32 FMAs, and a fixed-order reduction across the wave.
+// The NW waves of the workgroup take rows w, w + NW, ...; lane l takes blocks
+// l, l + 64, ....  The decode kernels use it where their fp16 conversion of
+// bf16 activations was inexact (values beyond fp16's range or off its
+// subnormal grid); it overwrites those rows' outputs.
+template <int NW>
+__device__ __forceinline__ void gemv_exact_rows_bf16(const uint16_t* x, const uint8_t* W, void* y,
+                                                     int y_f16, int m, int64_t n, int64_t k,
+                                                     int64_t row0, int nrows) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t nb = k / kQK;
+  const int64_t rb = nb * kBlockBytes;
+#pragma unroll 1
+  for (int r = wave; r < nrows; r += NW) {
+    const int64_t row = row0 + r;
+    const uint8_t* wr = W + row * rb;
+#pragma unroll 1
+    for (int mi = 0; mi < m; ++mi) {
+      const uint16_t* xr = x + static_cast<int64_t>(mi) * k;
+      float acc = 0.0f;
+      for (int64_t b = lane; b < nb; b += kWave) {
+        const uint8_t* blk = wr + b * kBlockBytes;
+        const float d = half_bits_to_float(static_cast<uint16_t>(blk[0] | (blk[1] << 8)));
+        const uint16_t* xb = xr + b * kQK;
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int c = blk[2 + j];
+          s = __builtin_fmaf(bf16_bits_to_float(xb[j]), static_cast<float>((c & 0xF) - 8), s);
+          s = __builtin_fmaf(bf16_bits_to_float(xb[j + 16]), static_cast<float>((c >> 4) - 8), s);
+        }
+        acc = __builtin_fmaf(d, s, acc);
+      }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      if (lane == 0) {
+        const int64_t o = static_cast<int64_t>(mi) * n + row;
+        if (y_f16) static_cast<half_t*>(y)[o] = static_cast<half_t>(acc);
+        else static_cast<float*>(y)[o] = acc;
+      }
+    }
+  }
+}
+
 
 }  // namespace q4

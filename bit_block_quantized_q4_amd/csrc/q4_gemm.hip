@@ -28,9 +28,21 @@
 //     step, with packed weights copied into LDS and dequantised in registers
 //     by the one wave that uses them; see its own comment.
 //   - gemm_tile_kernel: the generic LDS-tiled kernel for k % 64 != 0.
+//   - gemm_exact_kernel: the exact route (fp32 activations; see exact_tile128).
 // Launches run whole rounds of tiles on the compute units; a partial round's
 // columns run the same tiles with K split across workgroups (fp32 partials,
 // then splitk_reduce_kernel in split order).
+//
+// The fp16 tiles are exact up to fp32 summation only while every dequantised
+// weight and every activation is an fp16 value.  A block scale |d| > 8188
+// breaks the first (its largest element, code 0, dequantises to 8 |d| >
+// 65504, i.e. to +-inf), and bf16 activations outside fp16's range or off
+// its subnormal grid break the second (the bf16 staging pass writes such a
+// row as NaN).  Either makes the tile's fp32 accumulators non-finite, so
+// every fp16 kernel checks its accumulators once at the end and a workgroup
+// that finds a non-finite one recomputes its tile (and K range) on the exact
+// route from the original activations.  In-domain results are finite, so the
+// check never fires on them.
 #include "q4_device.hpp"
 
 namespace q4 {
@@ -46,12 +58,135 @@ constexpr int BN = 128;       // output features per workgroup
 constexpr int BK = kQK;       // one Q4_0 block per k step
 constexpr int LDK = BK + 8;   // padded LDS row (halves)
 
+// ------------------------------------------------------------------ exact route
+//
+// y = sum over blocks of sum_j x[j] (q_j - 8) d with the activations widened
+// exactly to fp32 (from fp32, fp16 or bf16) and the weights dequantised
+// exactly to fp32, contracted on v_mfma_f32_32x32x2_f32 (fp32 operands, fp32
+// accumulation): every product is formed from the exact operands, so the
+// error is fp32 summation error relative to sum |x w|, for every in-domain
+// input.  It is several times slower than the fp16 tiles.
+constexpr int kExLd = 17;                        // floats per LDS row (16 k + 1 pad)
+constexpr int kExLdsBytes = 2 * 128 * kExLd * 4;  // 17408
+
+__device__ __forceinline__ float load_x_f32(const void* x, DType xt, int64_t i) {
+  if (xt == DType::F32) return static_cast<const float*>(x)[i];
+  if (xt == DType::F16) return static_cast<float>(static_cast<const half_t*>(x)[i]);
+  return bf16_bits_to_float(static_cast<const uint16_t*>(x)[i]);
+}
+
+// One 128 x 128 output tile: activation rows r0 .. r0 + 127 (of m) against
+// weight rows (output columns) c0 .. c0 + 127 (of n), over the Q4_0 blocks
+// b0 .. b1 - 1 of K; y holds the tile's outputs at row stride ldy (final
+// outputs or fp32 split-K partials).  NTH threads (4 or 8 waves) stage each
+// half block (16 k) of x and of the dequantised weights in LDS; the waves
+// split the tile 2 x 2 (64 x 64 each, 2 x 2 products of 32 x 32) or, with
+// eight waves, 4 x 2 (32 x 64 each, 1 x 2 products), which keeps the
+// fallback's registers few where it is inlined into a large kernel.
+template <int NTH, typename YT>
+__device__ __forceinline__ void exact_tile128(const void* x, DType xt, int64_t ldx, const uint8_t* W,
+                                              int64_t rb, YT* y, int64_t ldy, int64_t m, int64_t n,
+                                              int64_t r0, int64_t c0, int64_t b0, int64_t b1,
+                                              float* lds) {
+  static_assert(NTH == 256 || NTH == 512, "four or eight waves");
+  constexpr int WVM = NTH == 512 ? 4 : 2;  // waves along the rows
+  constexpr int TI = 4 / WVM;              // 32-row products per wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  float* As = lds;
+  float* Bs = lds + 128 * kExLd;
+  float16_t acc[TI][2];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+#pragma unroll 1
+  for (int64_t b = b0; b < b1; ++b) {
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();  // the previous half's operand reads are done
+      for (int e = tid; e < 128 * 16; e += NTH) {
+        const int r = e >> 4, j = e & 15;
+        const int64_t gr = r0 + r, gc = c0 + r;
+        As[r * kExLd + j] = gr < m ? load_x_f32(x, xt, gr * ldx + kQK * b + 16 * h + j) : 0.0f;
+        float w = 0.0f;
+        if (gc < n) {
+          const uint8_t* blk = W + gc * rb + b * kBlockBytes;
+          const float d = half_bits_to_float(static_cast<uint16_t>(blk[0] | (blk[1] << 8)));
+          const int q = (blk[2 + j] >> (4 * h)) & 0xF;
+          w = static_cast<float>(q - 8) * d;
+        }
+        Bs[r * kExLd + j] = w;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int kc = 2 * kk + (lane >> 5);  // lane l supplies k = l / 32 of the pair
+        float a[TI], bv[2];
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+          a[i] = As[(wm * 32 * TI + 32 * i + (lane & 31)) * kExLd + kc];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bv[j] = Bs[(wn * 64 + 32 * j + (lane & 31)) * kExLd + kc];
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], bv[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+  // 32 x 32 accumulator layout: lane l holds column l % 32; register r holds
+  // row 8 (r / 4) + 4 (l / 32) + r % 4.
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = r0 + wm * 32 * TI + 32 * i + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
+        const int64_t col = c0 + wn * 64 + 32 * j + (lane & 31);
+        if (row < m && col < n) y[row * ldy + col] = static_cast<YT>(acc[i][j][r]);
+      }
+}
+
+// A BMT x BNT tile (multiples of 128) on the exact route, 128 x 128 at a time.
+template <int NTH, int BMT, int BNT, typename YT>
+__device__ __forceinline__ void exact_tile(const void* x, DType xt, int64_t ldx, const uint8_t* W, int64_t rb,
+                           YT* y, int64_t ldy, int64_t m, int64_t n, int64_t m0, int64_t n0,
+                           int64_t b0, int64_t b1, float* lds) {
+#pragma unroll 1
+  for (int ti = 0; ti < BMT / 128; ++ti)
+#pragma unroll 1
+    for (int tj = 0; tj < BNT / 128; ++tj)
+      exact_tile128<NTH, YT>(x, xt, ldx, W, rb, y, ldy, m, n, m0 + 128 * ti, n0 + 128 * tj, b0, b1,
+                             lds);
+}
+
+// Exact route as a kernel: one 128 x 128 tile per workgroup over all of K
+// (fp32 activations).
+template <typename YT>
+__global__ __launch_bounds__(256) void gemm_exact_kernel(const void* __restrict__ x, int xt,
+                                                         const uint8_t* __restrict__ W,
+                                                         YT* __restrict__ y, int64_t m, int64_t n,
+                                                         int64_t k) {
+  __shared__ __attribute__((aligned(16))) float lds[kExLdsBytes / 4];
+  exact_tile128<256, YT>(x, static_cast<DType>(xt), k, W, (k / kQK) * kBlockBytes, y, n, m, n,
+                         static_cast<int64_t>(blockIdx.y) * 128, static_cast<int64_t>(blockIdx.x) * 128,
+                         0, k / kQK, lds);
+}
+
 template <typename YT>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, YT* __restrict__ y,
-    int64_t m, int64_t n, int64_t k) {
-  __shared__ __attribute__((aligned(16))) half_t As[BM][LDK];
-  __shared__ __attribute__((aligned(16))) half_t Bs[BN][LDK];
+    int64_t m, int64_t n, int64_t k, const void* __restrict__ xe, int xet) {
+  // xe / xet: the original activations, for the exact route.
+  constexpr int kTileLds = 2 * BM * LDK * 2 > kExLdsBytes ? 2 * BM * LDK * 2 : kExLdsBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t tsm[kTileLds];
+  half_t (*As)[LDK] = reinterpret_cast<half_t (*)[LDK]>(tsm);
+  half_t (*Bs)[LDK] = reinterpret_cast<half_t (*)[LDK]>(tsm + BM * LDK * 2);
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -133,16 +268,22 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
 
   // 32x32 accumulator layout: lane l holds column l % 32; register r holds
   // row 8 * (r / 4) + 4 * (l / 32) + r % 4.
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        const float v = acc[i][j][r];
+        bad |= !__builtin_isfinite(v);
         const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
         const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (row < m && col < n) y[row * n + col] = static_cast<YT>(acc[i][j][r]);
+        if (row < m && col < n) y[row * n + col] = static_cast<YT>(v);
       }
+  if (workgroup_any_flag(bad, reinterpret_cast<uint32_t*>(tsm)))
+    exact_tile128<256, YT>(xe, static_cast<DType>(xet), k, W, nb * kBlockBytes, y, n, m, n, m0, n0,
+                           0, nb, reinterpret_cast<float*>(tsm));
 }
 
 
@@ -169,10 +310,12 @@ struct WUnit {
 template <int BM, int BN, int WVM, int WVN, typename YT>
 __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, YT* __restrict__ y,
-    int64_t m, int64_t n, int64_t k, int64_t ldy, int kps, int64_t zstride) {
+    int64_t m, int64_t n, int64_t k, int64_t ldy, int kps, int64_t zstride,
+    const void* __restrict__ xe, int xet) {
   // k: full K (row strides).  Workgroups with blockIdx.z = z take the K steps
   // z kps .. min((z + 1) kps, k / 64) - 1 and write y + z zstride (a split-K
-  // partial when gridDim.z > 1).
+  // partial when gridDim.z > 1).  xe / xet: the original activations, for
+  // the exact route.
   constexpr int NTH = WVM * WVN * 64;       // threads
   constexpr int WM = BM / WVM, WN = BN / WVN;  // wave tile
   constexpr int TM = WM / 32, TN = WN / 32; // 32 x 32 products per wave
@@ -194,6 +337,7 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
   const int ks0 = static_cast<int>(blockIdx.z) * kps;
   const int nks_all = static_cast<int>(k / kBK);
   const int nks = nks_all - ks0 < kps ? nks_all - ks0 : kps;
+  const uint8_t* const W0 = W;
   x += static_cast<int64_t>(ks0) * kBK;
   W += static_cast<int64_t>(ks0) * 2 * kBlockBytes;
   y += static_cast<int64_t>(blockIdx.z) * zstride;
@@ -425,16 +569,24 @@ __global__ __launch_bounds__(WVM * WVN * 64, 1) void gemm_mfma_kernel(
   // row 8 * (r / 4) + 4 * (l / 32) + r % 4.  (Storing y transposed from
   // swapped operands, four columns per 8-byte store, measured slower: each
   // store then touches 32 rows.)
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        const float v = acc[i][j][r];
+        bad |= !__builtin_isfinite(v);
         const int64_t row = m0 + wm * WM + 32 * i + 8 * (r / 4) + 4 * kg + (r & 3);
         const int64_t col = n0 + wn * WN + 32 * j + (lane & 31);
-        if (row < m && col < n) y[row * ldy + col] = static_cast<YT>(acc[i][j][r]);
+        if (row < m && col < n) y[row * ldy + col] = static_cast<YT>(v);
       }
+  // A non-finite accumulator: this tile's outputs are rewritten on the exact route.
+  if (workgroup_any_flag(bad, reinterpret_cast<uint32_t*>(smem)))
+    exact_tile<NTH, BM, BN, YT>(xe, static_cast<DType>(xet), k, W0, rb, y, ldy, m, n, m0, n0,
+                                2 * static_cast<int64_t>(ks0), 2 * static_cast<int64_t>(ks0 + nks),
+                                reinterpret_cast<float*>(smem));
 }
 
 // ------------------------------------------------------------------ slice-K
@@ -471,9 +623,11 @@ static_assert(4 * 128 * kSkRedCol * 4 <= kSkLds, "reduction buffer");
 template <typename YT>
 __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, YT* __restrict__ y,
-    int64_t m, int64_t n, int64_t k, int64_t ldy, int kps, int64_t zstride) {
+    int64_t m, int64_t n, int64_t k, int64_t ldy, int kps, int64_t zstride,
+    const void* __restrict__ xe, int xet) {
   // k: full K (row strides).  Workgroups with blockIdx.z = z take the k steps
   // z kps .. min((z + 1) kps, k / 64) - 1 (kps % 4 == 0) and write y + z zstride.
+  // xe / xet: the original activations, for the exact route.
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSkLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -486,6 +640,7 @@ __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
   const int nks_all = static_cast<int>(k / kBK);
   const int nks = nks_all - ks0 < kps ? nks_all - ks0 : kps;  // a multiple of 4
   const int nss = nks >> 2;
+  const uint8_t* const W0 = W;
   x += static_cast<int64_t>(ks0) * kBK;
   W += static_cast<int64_t>(ks0) * 2 * kBlockBytes;
   y += static_cast<int64_t>(blockIdx.z) * zstride;
@@ -717,6 +872,7 @@ __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
   const int rb4 = tid & 7, cb4 = tid >> 3;
   const int64_t col = n0 + 4 * cb4;
   const bool vec_ok = (ldy & 3) == 0 && col + 3 < n;
+  bool bad = false;  // a non-finite sum (then the exact route rewrites the tile)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -735,6 +891,10 @@ __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         sc[c] += *reinterpret_cast<const float4_t*>(red + (w * 128 + 4 * cb4 + c) * kSkRedCol + 4 * rb4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bad |= !__builtin_isfinite(sc[c][r]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t row = m0 + 32 * i + 4 * rb4 + r;
@@ -756,17 +916,27 @@ __global__ __launch_bounds__(256, 1) void gemm_slicek_kernel(
     }
     __syncthreads();
   }
+  if (workgroup_any_flag(bad, reinterpret_cast<uint32_t*>(smem)))
+    exact_tile128<256, YT>(xe, static_cast<DType>(xet), k, W0, rb, y, ldy, m, n, m0, n0,
+                           2 * static_cast<int64_t>(ks0), 2 * static_cast<int64_t>(ks0 + nks),
+                           reinterpret_cast<float*>(smem));
 }
 
 // Output columns c0 .. c0 + nc - 1 (weight rows c0 ..) into yc (their first
 // column, row stride ldy); with splits > 1, split z of K goes to yc + z zstride.
+// The original activations (the exact route's input): a pointer and dtype.
+struct XSrc {
+  const void* p;
+  int dt;
+};
+
 template <int BM, int BN, int WVM, int WVN, typename YT>
 hipError_t launch_tiled(const half_t* x, const uint8_t* packed, int64_t c0, int64_t nc, YT* yc,
                         int64_t m, int64_t k, int64_t ldy, int splits, int kps, int64_t zstride,
-                        hipStream_t s) {
+                        XSrc xe, hipStream_t s) {
   const uint8_t* w = packed + c0 * ((k / kQK) * kBlockBytes);
   void* argv[] = {const_cast<const half_t**>(&x), const_cast<const uint8_t**>(&w), &yc, &m,
-                  &nc, &k, &ldy, &kps, &zstride};
+                  &nc, &k, &ldy, &kps, &zstride, &xe.p, &xe.dt};
   const dim3 grid(static_cast<unsigned>((nc + BN - 1) / BN), static_cast<unsigned>((m + BM - 1) / BM),
                   static_cast<unsigned>(splits));
   return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, WVM, WVN, YT>),
@@ -776,10 +946,10 @@ hipError_t launch_tiled(const half_t* x, const uint8_t* packed, int64_t c0, int6
 template <typename YT>
 hipError_t launch_slicek(const half_t* x, const uint8_t* packed, int64_t c0, int64_t nc, YT* yc,
                          int64_t m, int64_t k, int64_t ldy, int splits, int kps, int64_t zstride,
-                         hipStream_t s) {
+                         XSrc xe, hipStream_t s) {
   const uint8_t* w = packed + c0 * ((k / kQK) * kBlockBytes);
   void* argv[] = {const_cast<const half_t**>(&x), const_cast<const uint8_t**>(&w), &yc, &m,
-                  &nc, &k, &ldy, &kps, &zstride};
+                  &nc, &k, &ldy, &kps, &zstride, &xe.p, &xe.dt};
   const dim3 grid(static_cast<unsigned>((nc + 127) / 128), static_cast<unsigned>((m + 127) / 128),
                   static_cast<unsigned>(splits));
   return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_slicek_kernel<YT>), grid, dim3(256),
@@ -853,22 +1023,22 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
 
 template <typename YT>
 hipError_t dispatch_tiled(const half_t* x, const uint8_t* packed, YT* y, int64_t m, int64_t n,
-                          int64_t k, void* workspace, hipStream_t s) {
+                          int64_t k, void* workspace, XSrc xe, hipStream_t s) {
   const GemmPlan p = gemm_plan(m, n, k);
   const int nks = static_cast<int>(k / kBK);
-  hipError_t e = p.big      ? launch_tiled<256, 256, 2, 4, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, s)
-                 : p.slicek ? launch_slicek<YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, s)
-                            : launch_tiled<128, 128, 2, 2, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, s);
+  hipError_t e = p.big      ? launch_tiled<256, 256, 2, 4, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, xe, s)
+                 : p.slicek ? launch_slicek<YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, xe, s)
+                            : launch_tiled<128, 128, 2, 2, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, xe, s);
   if (e != hipSuccess || p.n_main == n) return e;
   // Tail: split z of K writes part[z], m x nt with row stride nt.
   const int64_t nt = n - p.n_main;
   float* part = static_cast<float*>(workspace);
   e = p.tail_slicek ? launch_slicek<float>(x, packed, p.n_main, nt, part, m, k, nt, p.splits,
-                                            p.kps, m * nt, s)
+                                            p.kps, m * nt, xe, s)
       : p.big        ? launch_tiled<256, 256, 2, 4, float>(x, packed, p.n_main, nt, part, m, k, nt,
-                                                          p.splits, p.kps, m * nt, s)
+                                                          p.splits, p.kps, m * nt, xe, s)
                      : launch_tiled<128, 128, 2, 2, float>(x, packed, p.n_main, nt, part, m, k, nt,
-                                                          p.splits, p.kps, m * nt, s);
+                                                          p.splits, p.kps, m * nt, xe, s);
   if (e != hipSuccess) return e;
   const int64_t quads = m * nt / 4;
   YT* yt = y + p.n_main;
@@ -886,25 +1056,42 @@ namespace {
 // Converted bf16 activations occupy the workspace's first bytes.
 int64_t bf16_stage_bytes(int64_t m, int64_t k) { return (m * k * 2 + 255) / 256 * 256; }
 
-// bf16 activations -> fp16 (round to nearest even; exact for every value fp16
-// represents), eight values per thread per step.  ndw (dwords) is a multiple
-// of 4 (k is a multiple of 32), and both buffers are 16-byte aligned.
-__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint32_t* __restrict__ x,
-                                                          uint32_t* __restrict__ out, int64_t ndw) {
-  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  const int64_t nq = ndw / 4;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < nq; i += stride) {
-    u32x4_t v = reinterpret_cast<const u32x4_t*>(x)[i];
+// bf16 activations -> fp16 rows (round to nearest even), one wave per row,
+// four rows per workgroup.  A row that holds any value fp16 cannot represent
+// exactly (beyond its range, or off its subnormal grid) is written entirely
+// as NaN instead: every tile and K split that reads it then ends with
+// non-finite accumulators and is recomputed on the exact route from the bf16
+// original.  Both buffers are 16-byte aligned and k % 32 == 0.
+__global__ __launch_bounds__(256) void bf16_rows_to_f16_kernel(const uint16_t* __restrict__ x,
+                                                               uint16_t* __restrict__ out,
+                                                               int64_t m, int64_t k) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= m) return;  // whole wave
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * k);
+  u32x4* dst = reinterpret_cast<u32x4*>(out + row * k);
+  const int64_t np = k / 8;  // 16-byte pieces
+  bool inexact = false;
+  for (int64_t p = lane; p < np; p += kWave) {
+    u32x4 v = src[p];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
-    reinterpret_cast<u32x4_t*>(out)[i] = v;
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t h = bf16x2_to_f16x2(v[e]);
+      inexact |= !f16x2_holds_bf16x2(h, v[e]);
+      v[e] = h;
+    }
+    dst[p] = v;
+  }
+  if (__ballot(inexact) != 0) {
+    const u32x4 qnan = {0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u};
+    for (int64_t p = lane; p < np; p += kWave) dst[p] = qnan;  // after this lane's own stores
   }
 }
 
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, DType xt) {
+  if (xt == DType::F32) return 0;  // the exact route needs no workspace
   const size_t tiles = gemm_plan(m, n, k).ws_bytes;
   return xt == DType::BF16 ? static_cast<size_t>(bf16_stage_bytes(m, k)) + tiles : tiles;
 }
@@ -912,41 +1099,51 @@ size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, DType xt) {
 hipError_t launch_gemm(const void* x, DType xt, const uint8_t* packed, void* y,
                        DType yt, int64_t m, int64_t n, int64_t k, void* workspace,
                        hipStream_t s) {
+  const dim3 grid128(static_cast<unsigned>((n + 127) / 128), static_cast<unsigned>((m + 127) / 128));
+  if (xt == DType::F32) {
+    // fp32 activations: the exact route (fp32 matrix cores) for every tile.
+    int xti = static_cast<int>(xt);
+    void* argv[] = {const_cast<void**>(&x), &xti, const_cast<const uint8_t**>(&packed), &y,
+                    &m, &n, &k};
+    const void* fn = yt == DType::F16 ? reinterpret_cast<const void*>(&gemm_exact_kernel<half_t>)
+                                      : reinterpret_cast<const void*>(&gemm_exact_kernel<float>);
+    return hipLaunchKernel(fn, grid128, dim3(256), argv, 0, s);
+  }
   const half_t* xp = static_cast<const half_t*>(x);
+  const XSrc xe{x, static_cast<int>(xt)};
   if (xt == DType::BF16) {
-    // Stage the activations as fp16 in the workspace, then run the fp16 path
-    // on them with the rest of the workspace.
+    // Stage the activations as fp16 rows in the workspace (NaN rows where
+    // fp16 cannot hold them exactly), then run the fp16 path on them with the
+    // rest of the workspace; the exact route reads the bf16 original.
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    const int64_t ndw = m * k / 2;
-    const int64_t blocks = (ndw / 4 + 255) / 256;
-    const dim3 grid(static_cast<unsigned>(blocks < 4096 ? blocks : 4096));
-    const uint32_t* src = static_cast<const uint32_t*>(x);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(ws);
-    int64_t nd = ndw;
-    void* argv[] = {&src, &dst, &nd};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bf16_to_f16_kernel), grid,
-                                         dim3(256), argv, 0, s);
+    const uint16_t* src = static_cast<const uint16_t*>(x);
+    uint16_t* dst = reinterpret_cast<uint16_t*>(ws);
+    int64_t mm = m, kk = k;
+    void* argv[] = {&src, &dst, &mm, &kk};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bf16_rows_to_f16_kernel),
+                                         dim3(static_cast<unsigned>((m + 3) / 4)), dim3(256), argv,
+                                         0, s);
     if (e != hipSuccess) return e;
     xp = reinterpret_cast<const half_t*>(ws);
     workspace = gemm_plan(m, n, k).ws_bytes > 0 ? ws + bf16_stage_bytes(m, k) : nullptr;
   }
   if (k % kBK == 0) {
     if (yt == DType::F16)
-      return dispatch_tiled(xp, packed, static_cast<half_t*>(y), m, n, k, workspace, s);
-    return dispatch_tiled(xp, packed, static_cast<float*>(y), m, n, k, workspace, s);
+      return dispatch_tiled(xp, packed, static_cast<half_t*>(y), m, n, k, workspace, xe, s);
+    return dispatch_tiled(xp, packed, static_cast<float*>(y), m, n, k, workspace, xe, s);
   }
-  const dim3 grid(static_cast<unsigned>((n + BN - 1) / BN),
-                  static_cast<unsigned>((m + BM - 1) / BM));
+  const void* xev = xe.p;
+  int xet = xe.dt;
   if (yt == DType::F16) {
     half_t* yp = static_cast<half_t*>(y);
-    void* argv[] = {&xp, const_cast<const uint8_t**>(&packed), &yp, &m, &n, &k};
+    void* argv[] = {&xp, const_cast<const uint8_t**>(&packed), &yp, &m, &n, &k, &xev, &xet};
     return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_tile_kernel<half_t>),
-                           grid, dim3(256), argv, 0, s);
+                           grid128, dim3(256), argv, 0, s);
   }
   float* yp = static_cast<float*>(y);
-  void* argv[] = {&xp, const_cast<const uint8_t**>(&packed), &yp, &m, &n, &k};
+  void* argv[] = {&xp, const_cast<const uint8_t**>(&packed), &yp, &m, &n, &k, &xev, &xet};
   return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_tile_kernel<float>),
-                         grid, dim3(256), argv, 0, s);
+                         grid128, dim3(256), argv, 0, s);
 }
 
 }  // namespace q4

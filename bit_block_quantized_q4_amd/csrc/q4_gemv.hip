@@ -402,7 +402,9 @@ __host__ __device__ inline BalLds bal_lds(int m, int64_t k, int rg, int nw, int 
 }
 
 // XB: the activations arrive as bf16 and are converted to fp16 in LDS, in
-// place, once staged (exact for every value fp16 represents).
+// place, once staged (exact for every value fp16 represents); if any
+// conversion was not exact, the workgroup's rows are recomputed at the end on
+// the exact route (gemv_exact_rows_bf16).
 template <int NW, int P, int MR, bool XB>
 __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, void* __restrict__ y,
@@ -552,6 +554,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
   // bf16 activations: every wave's x copies have landed (the barrier before
   // this); convert the staged rows to fp16 in place, then a second barrier
   // (task copies stay in flight through it).
+  bool inexact = false;  // a bf16 activation that fp16 does not hold exactly
   auto convert_x = [&]() {
     if constexpr (XB) {
       // 16-byte pieces (eight values), four per thread in flight
@@ -566,14 +569,22 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[u][e] = bf16x2_to_f16x2(v[u][e]);
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t h = bf16x2_to_f16x2(v[u][e]);
+            inexact |= !f16x2_holds_bf16x2(h, v[u][e]);
+            v[u][e] = h;
+          }
           xq[i + u * kT] = v[u];
         }
       }
       for (; i < nq; i += kT) {
         u32x4 v = xq[i];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t h = bf16x2_to_f16x2(v[e]);
+          inexact |= !f16x2_holds_bf16x2(h, v[e]);
+          v[e] = h;
+        }
         xq[i] = v;
       }
       wait_lgkm0();
@@ -649,6 +660,10 @@ __global__ __launch_bounds__(NW * kWave) void gemv_bal_kernel(
     const int64_t off = static_cast<int64_t>(mo) * n + r0 + rl;
     if (y_f16) static_cast<half_t*>(y)[off] = static_cast<half_t>(sum);
     else static_cast<float*>(y)[off] = sum;
+  }
+  if constexpr (XB) {
+    if (workgroup_any_flag(inexact, reinterpret_cast<uint32_t*>(bal_smem)))
+      gemv_exact_rows_bf16<NW>(reinterpret_cast<const uint16_t*>(x), W, y, y_f16, m, n, k, r0, nrows);
   }
 }
 

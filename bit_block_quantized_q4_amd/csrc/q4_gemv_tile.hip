@@ -97,7 +97,9 @@ struct TileGeo {
 // n - 1 and are not stored); otherwise R = rows < 16 T rows and only those
 // are copied (a run-time bound on the copies).  XB: the activations are bf16;
 // each operand fragment is converted to fp16 in registers after its LDS read
-// (round to nearest even, exact for every value fp16 represents).  (Having
+// (round to nearest even, exact for every value fp16 represents) and checked
+// to be exact; if any conversion of the workgroup was not, its rows are
+// recomputed on the exact route (gemv_exact_rows_bf16).  (Having
 // the copying waves convert their own pieces in LDS before the phase barrier
 // instead measured slower: 12.3 against 8.9 us at 5120 x 5120, m = 16, as it
 // delays the barrier and the next phase's copies.)
@@ -200,6 +202,7 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
       }
   }
   const UnpackConsts kc = make_unpack_consts();
+  bool inexact = false;  // a bf16 activation that fp16 does not hold exactly
   float4_t acc[T][AT];
 #pragma unroll
   for (int i = 0; i < T; ++i)
@@ -218,7 +221,11 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
         u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         if constexpr (XB) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = bf16x2_to_f16x2(a[e]);
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t h = bf16x2_to_f16x2(a[e]);
+            inexact |= !f16x2_holds_bf16x2(h, a[e]);
+            a[e] = h;
+          }
         }
         A[j][t] = __builtin_bit_cast(half8_t, a);
       }
@@ -323,6 +330,11 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
       if (y_f16) static_cast<half_t*>(y)[off] = static_cast<half_t>(sum);
       else static_cast<float*>(y)[off] = sum;
     }
+  }
+  if constexpr (XB) {
+    if (workgroup_any_flag(inexact, reinterpret_cast<uint32_t*>(tsm)))
+      gemv_exact_rows_bf16<NW + NP>(reinterpret_cast<const uint16_t*>(x), W, y, y_f16, m, n, k, row0,
+                                    rv);
   }
 }
 

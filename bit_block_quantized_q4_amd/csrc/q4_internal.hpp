@@ -45,6 +45,15 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Whether the fp16 pair h (from bf16x2_to_f16x2) denotes exactly the bf16
+// pair v: false where fp16 overflowed or rounded (out of fp16's range or off
+// its subnormal grid) and for NaN.
+__device__ __forceinline__ bool f16x2_holds_bf16x2(uint32_t h, uint32_t v) {
+  const half2_t hh = __builtin_bit_cast(half2_t, h);
+  return static_cast<float>(hh[0]) == __builtin_bit_cast(float, v << 16) &&
+         static_cast<float>(hh[1]) == __builtin_bit_cast(float, v & 0xFFFF0000u);
+}
+
 // Launchers (return the launch status; never synchronise).
 hipError_t launch_quantize(const void* w, DType wt, int64_t n, int64_t k,
                            uint8_t* packed, hipStream_t s);

@@ -47,7 +47,8 @@
  *     non-NULL (Q4_ERR_INVALID_ARG); outputs must not overlap inputs
  *     (Q4_ERR_INVALID_ARG);
  *   - shapes: n >= 1, m >= 1, k >= 32 and k % 32 == 0, and n * k below 2^40
- *     (Q4_ERR_SHAPE);
+ *     (Q4_ERR_SHAPE); for q4_gemv and q4_gemm also k <= 2^24 (the kernels
+ *     address a tile's activation rows with 32-bit per-lane byte offsets);
  *   - inputs must be finite; weights must satisfy |w| < 65520 * 8 so that d
  *     is finite.  This is not checked on the device.
  */
@@ -112,15 +113,15 @@ q4_status q4_quantize(const void *w, int w_dtype, int64_t n, int64_t k,
  * 1 <= m <= Q4_GEMV_MAX_M (the page's batched decode stage).  x is Q4_F32,
  * Q4_F16 or Q4_BF16, y is Q4_F32 or Q4_F16.  Every output is the fp32 sum
  * over blocks of d times the block dot product of x with (q - 8), rounded
- * once to the output dtype.  The block dot products are exact for m <= 4;
- * for larger m with fp16 x and k a multiple of 512 they come from fp16 matrix
- * cores fed the codes as fp16 subnormals, within about 1e-6 of exact relative
- * to their magnitude sum.  bf16 x with k a multiple of 512 is converted to
- * fp16 inside the kernel (round to nearest even) and then takes the fp16
- * path: exact for every bf16 value fp16 represents, which includes every
- * value with 2^-14 <= |x| <= 65504 (larger magnitudes overflow; smaller ones
- * are rounded to fp16's subnormal grid); other bf16 shapes are widened
- * exactly to fp32.  Streams each packed byte from memory once per call. */
+ * once to the output dtype.  The block products take the codes as exact
+ * integers q - 8, so each product x (q - 8) is exact and the error is fp32
+ * summation error relative to sum |x w|, for every in-domain input.  bf16
+ * x with k a multiple of 512 is converted to fp16 inside the kernel (round
+ * to nearest even); a workgroup whose conversion was inexact anywhere (a
+ * value beyond fp16's range or off its subnormal grid) recomputes its
+ * outputs with x widened exactly to fp32, so the result is exact for every
+ * bf16 value; other bf16 shapes are widened exactly to fp32.  Streams each
+ * packed byte from memory once per call. */
 q4_status q4_gemv(const void *x, int x_dtype, const void *packed, void *y,
                   int y_dtype, int64_t m, int64_t n, int64_t k,
                   q4_stream_t stream);
@@ -129,25 +130,29 @@ q4_status q4_gemv(const void *x, int x_dtype, const void *packed, void *y,
  * when none). */
 size_t q4_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 
-/* As q4_gemm_workspace_size for activations of dtype x_dtype (Q4_F16 or
- * Q4_BF16; 0 for any other dtype or an invalid shape).  bf16 activations add
+/* As q4_gemm_workspace_size for activations of dtype x_dtype (0 for fp32
+ * activations, an unknown dtype or an invalid shape).  bf16 activations add
  * m * k * 2 bytes (rounded up to 256), where they are staged as fp16. */
 size_t q4_gemm_workspace_size_dt(int64_t m, int64_t n, int64_t k, int x_dtype);
 
 /* Prefill GEMM: y[m][n] = x[m][k] . dequant(packed)^T for any m >= 1 (the
- * page's GPU path onto matrix cores): weight tiles are dequantised to fp16
- * (w = (q - 8) * d rounded once) and contracted on fp16 matrix cores with fp32
- * accumulation.  Because the weights are rounded to fp16, every block scale
- * must satisfy |d| <= 8188 (every dequantised weight within the fp16 range,
- * |w| <= 65504); larger scales give infinite outputs (not checked; q4_gemv has
- * no such limit).  x is Q4_F16 or Q4_BF16; y is Q4_F32 or Q4_F16.  bf16
- * activations are first converted to fp16 into the workspace (round to
- * nearest even; exact for every value fp16 represents, every value with
- * 2^-14 <= |x| <= 65504 among them).  `workspace` must hold
- * q4_gemm_workspace_size_dt(m, n, k, x_dtype) bytes (it may be NULL when that
- * is 0) and must not overlap x, y or packed; its contents on entry are
- * ignored.  A prompt processed in row chunks passes x + c*rows*k and
- * y + c*rows*n for chunk c. */
+ * page's GPU path onto matrix cores).  x is Q4_F32, Q4_F16 or Q4_BF16; y is
+ * Q4_F32 or Q4_F16.
+ *   - fp16 and bf16 activations: weight tiles are dequantised to fp16
+ *     (w = (q - 8) * d rounded once) and contracted on fp16 matrix cores
+ *     with fp32 accumulation; bf16 activations are first staged as fp16 in
+ *     the workspace (round to nearest even).  Where that is not exact -- a
+ *     block scale |d| > 8188, whose dequantised weights leave fp16's range,
+ *     or a bf16 activation fp16 cannot hold -- the affected output tiles come
+ *     out non-finite inside the kernel and are recomputed there on the exact
+ *     route below, so every in-domain input gives a result within tolerance.
+ *   - fp32 activations take the exact route for every tile: activations and
+ *     dequantised weights in fp32 on fp32 matrix cores (several times slower
+ *     than the fp16 tiles).
+ * `workspace` must hold q4_gemm_workspace_size_dt(m, n, k, x_dtype) bytes (it
+ * may be NULL when that is 0) and must not overlap x, y or packed; its
+ * contents on entry are ignored.  A prompt processed in row chunks passes
+ * x + c*rows*k and y + c*rows*n for chunk c. */
 q4_status q4_gemm(const void *x, int x_dtype, const void *packed, void *y,
                   int y_dtype, int64_t m, int64_t n, int64_t k,
                   void *workspace, size_t workspace_bytes,

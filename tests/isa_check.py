@@ -31,13 +31,19 @@ def kernels(asm_text, name_pattern):
 def metadata(asm_text):
     """name -> dict of the kernel descriptor fields we check."""
     meta = {}
-    for name, body in re.findall(r"\.name:\s+(\S+)(.*?)(?=\n  - |\Z)", asm_text, re.S):
-        def get(key):
-            m = re.search(r"\." + key + r":\s+(\S+)", body)
-            return int(m.group(1)) if m else None
-        meta[name] = {"private_segment_fixed_size": get("private_segment_fixed_size"),
-                      "vgpr_spill_count": get("vgpr_spill_count"),
-                      "vgpr_count": get("vgpr_count")}
+    m = re.search(r"amdhsa\.kernels:(.*?)(?:\n\S|\Z)", asm_text, re.S)
+    section = m.group(1) if m else asm_text
+    for entry in re.split(r"\n  - ", section):
+        nm = re.search(r"\.name:\s+(\S+)", entry)
+        if not nm:
+            continue
+        def get(key, body=entry):
+            g = re.search(r"\." + key + r":\s+(\S+)", body)
+            return int(g.group(1)) if g else None
+        meta[nm.group(1)] = {"private_segment_fixed_size": get("private_segment_fixed_size"),
+                             "group_segment_fixed_size": get("group_segment_fixed_size"),
+                             "vgpr_spill_count": get("vgpr_spill_count"),
+                             "vgpr_count": get("vgpr_count")}
     return meta
 
 

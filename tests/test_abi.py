@@ -89,7 +89,7 @@ def test_gemv_argument_checks(q4lib):
 
 def test_gemm_argument_checks(q4lib):
     f = q4lib.lib().q4_gemm
-    assert f(A, F32, B, C, F16, 64, 8, 32, None, 0, None) == DTYPE  # fp16 activations only
+    assert f(A, 7, B, C, F16, 64, 8, 32, None, 0, None) == DTYPE
     assert f(A, F16, B, C, F16, 0, 8, 32, None, 0, None) == SHAPE
     assert f(A, F16, B, C, F16, 64, 8, 33, None, 0, None) == SHAPE
     assert f(A, F16, B, C, 3, 64, 8, 32, None, 0, None) == DTYPE
@@ -102,7 +102,8 @@ def test_gemm_argument_checks(q4lib):
     needb = q4lib.q4_gemm_workspace_size_dt(64, 8, 32, BF16)
     assert needb >= need + 64 * 32 * 2
     assert q4lib.q4_gemm_workspace_size_dt(64, 8, 32, F16) == need
-    assert q4lib.q4_gemm_workspace_size_dt(64, 8, 32, F32) == 0
+    assert q4lib.q4_gemm_workspace_size_dt(64, 8, 32, F32) == 0   # the exact route needs none
+    assert q4lib.q4_gemm_workspace_size_dt(64, 8, 32, 7) == 0
     assert f(A, BF16, B, C, F16, 64, 8, 32, None, 0, None) == WORKSPACE
     assert f(A, BF16, B, C, F16, 64, 8, 32, 0x60000000, needb - 1, None) == WORKSPACE
     assert f(A, BF16, B, C, F16, 64, 8, 32, 0x60000008, needb, None) == ALIGN
@@ -110,12 +111,24 @@ def test_gemm_argument_checks(q4lib):
     assert f(A, BF16, B, C, BF16, 64, 8, 32, 0x60000000, needb, None) == DTYPE
 
 
+def test_matmul_k_limit(q4lib):
+    """k above 2^24 is refused (32-bit per-lane offsets inside the kernels)."""
+    k_ok, k_big = 1 << 24, (1 << 24) + 32
+    assert q4lib.lib().q4_gemv(A, F16, B, C, F16, 1, 1, k_big, None) == SHAPE
+    assert q4lib.lib().q4_gemm(A, F16, B, C, F16, 1, 1, k_big, None, 0, None) == SHAPE
+    assert q4lib.lib().q4_gemm_noalloc(A, F16, B, C, F16, 1, 1, k_big, None) == SHAPE
+    assert q4lib.q4_gemm_workspace_size_dt(1, 1, k_big, BF16) == 0
+    assert q4lib.q4_gemm_workspace_size_dt(1, 1, k_ok, BF16) >= k_ok * 2
+    # the quantiser and the packed size have no such limit
+    assert q4lib.q4_packed_size(1, k_big) == (k_big // 32) * 18
+
+
 def test_gemm_noalloc_argument_checks(q4lib):
     """q4_gemm_noalloc validates like q4_gemm and refuses, before any launch,
     calls whose workspace need exceeds its fixed scratch array."""
     f = q4lib.lib().q4_gemm_noalloc
     assert f(None, F16, B, C, F16, 64, 8, 32, None) == INVALID
-    assert f(A, F32, B, C, F16, 64, 8, 32, None) == DTYPE
+    assert f(A, 7, B, C, F16, 64, 8, 32, None) == DTYPE
     assert f(A, F16, B, C, F16, 0, 8, 32, None) == SHAPE
     assert f(A + 8, F16, B, C, F16, 64, 8, 32, None) == ALIGN
     assert f(A, F16, B, A, F16, 64, 8, 32, None) == INVALID

@@ -302,3 +302,80 @@ def test_edge_case_weights_main_kernels(q4lib, gpu, m, n, k):
         import torch
         g = to_host(q4lib.q4_gemm(to_dev(x, gpu), pd, y_dtype=torch.float32, n=n, k=k))
         assert_matmul_close(g, x, packed, n, k, what=f"edge {name} m{m} n{n} k{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 100, 64), (37, 300, 1056), (300, 520, 2048),
+                                   (1100, 700, 1024), (256, 200, 96)])
+@pytest.mark.parametrize("ydt", ["f16", "f32"])
+def test_fp32_activations(q4lib, gpu, m, n, k, ydt):
+    """fp32 activations take the exact route (activations and dequantised
+    weights in fp32 on fp32 matrix cores); every output checked."""
+    w = synth.random_weights(17 * m + n + k, n, k, "student_t")
+    x = synth.random_activations(19 * m + k, m, k, "f32")
+    packed = oracle.quantize(w)
+    g = run_gemm(q4lib, x, packed, n, k, ydt, gpu)
+    assert_matmul_close(g, x, packed, n, k, what=f"fp32 x m{m} n{n} k{k} -> {ydt}")
+
+
+# Every GEMM kernel: the generic kernel (k % 64 != 0), 128 x 128 output-split
+# tiles (k = 768), slice-K tiles with and without a split-K tail, 256 x 256
+# tiles with a split-K tail.
+ALL_GEMM_KERNELS = [(160, 300, 96 * 3), (200, 300, 768), (256, 4100, 1536), (300, 11000, 1024),
+                    (1100, 4100, 1536), (2048, 8448, 5120)]
+
+
+@pytest.mark.parametrize("m,n,k", ALL_GEMM_KERNELS)
+def test_scales_beyond_the_fp16_weight_range(q4lib, gpu, m, n, k):
+    """Block scales far above 8188 (weights up to 5e5, the top of the domain):
+    the fp16 dequantised tile overflows there, the tile's accumulators come out
+    non-finite and the workgroup recomputes its tile on the exact route.
+    Corner-case rows (a tenth of the blocks near the top of the domain) and a
+    weight whose every block is beyond fp16; every output checked."""
+    import torch
+    for name, w in (("edge", edge_rows(151 + k, n, k, 5.0e5)),
+                    ("all-big", np.clip(synth.random_weights(157 + k, n, k, "normal") * np.float32(5e6),
+                                        -5e5, 5e5).astype(np.float32))):
+        packed = oracle.quantize(w)
+        d, _ = oracle.unpack(packed, n, k)
+        assert np.abs(d.astype(np.float32)).max() > 8188
+        x = synth.random_activations(163 + m, m, k, "f16")
+        g = to_host(q4lib.q4_gemm(to_dev(x, gpu), to_dev(packed, gpu), y_dtype=torch.float32,
+                                  n=n, k=k))
+        assert np.isfinite(g).all()
+        assert_matmul_close(g, x, packed, n, k, what=f"big d {name} m{m} n{n} k{k}")
+
+
+def bf16_beyond_fp16(seed, m, k):
+    """bf16 activations, N(0, 1) except in a few rows that also hold values
+    fp16 cannot represent: magnitudes up to 1e20 and down to 1e-30, and values
+    between fp16 subnormals."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, size=min(m, 5), replace=False)]))
+    for i, r in enumerate(rows):
+        cols = rng.choice(k, size=min(k, 9), replace=False)
+        kind = i % 3
+        if kind == 0:
+            x[r, cols] = np.float32(1e20) * rng.uniform(0.5, 1.0, size=len(cols)).astype(np.float32)
+        elif kind == 1:
+            x[r, cols] = np.float32(1e-30) * rng.uniform(0.5, 1.0, size=len(cols)).astype(np.float32)
+        else:
+            x[r, cols] = np.float32(1.5 * 2.0 ** -25)   # halfway between fp16 subnormals
+        x[r, cols] *= np.where(rng.random(len(cols)) < 0.5, -1, 1).astype(np.float32)
+    return synth.bf16_bits(x), rows
+
+
+@pytest.mark.parametrize("m,n,k", ALL_GEMM_KERNELS)
+def test_bf16_activations_beyond_the_fp16_range(q4lib, gpu, m, n, k):
+    """bf16 rows holding values fp16 cannot represent are staged as NaN rows, so
+    every tile and K split that reads them is recomputed on the exact route
+    from the bf16 values; every output checked (rows with 1e20 give outputs
+    near 1e19, so the output is fp32)."""
+    import torch
+    w = synth.random_weights(167 + k, n, k, "student_t")
+    packed = oracle.quantize(w)
+    xb, rows = bf16_beyond_fp16(173 + m, m, k)
+    y = to_host(q4lib.q4_gemm(to_dev_bf16(xb, gpu), to_dev(packed, gpu), y_dtype=torch.float32,
+                              n=n, k=k))
+    assert np.isfinite(y).all()
+    assert_matmul_close(y, oracle.widen_bf16(xb), packed, n, k, what=f"bf16 range m{m} n{n} k{k}")

@@ -419,3 +419,22 @@ def test_wide_range_activations(q4lib, gpu, m):
         packed = oracle.quantize(w)
         g = run_gemv(q4lib, x, packed, n, k, "f32", gpu)
         assert_matmul_close(g, x, packed, n, k, what=f"wide m{m} n{n} k{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 300, 2048), (3, 1000, 5120), (4, 129, 512),
+                                   (5, 4097, 1536), (10, 5120, 5120), (16, 300, 1024),
+                                   (32, 520, 2048), (7, 70, 96)])
+def test_bf16_activations_beyond_the_fp16_range(q4lib, gpu, m, n, k):
+    """bf16 activations fp16 cannot hold (up to 1e20, down to 1e-30, between
+    fp16 subnormals): the balanced (m <= 4) and tile (m >= 5) kernels detect
+    the inexact conversion and recompute the workgroup's rows on the exact
+    route; the general kernel (k = 96) widens exactly anyway.  Every output."""
+    import torch
+    from test_gpu_gemm import bf16_beyond_fp16
+    w = synth.random_weights(181 + k, n, k, "student_t")
+    packed = oracle.quantize(w)
+    xb, _ = bf16_beyond_fp16(191 + m, m, k)
+    y = to_host(q4lib.q4_gemv(to_dev_bf16(xb, gpu), to_dev(packed, gpu), y_dtype=torch.float32,
+                              n=n, k=k))
+    assert np.isfinite(y).all()
+    assert_matmul_close(y, oracle.widen_bf16(xb), packed, n, k, what=f"bf16 range m{m} n{n} k{k}")

@@ -48,6 +48,19 @@ def test_no_scratch_or_spills(src):
         assert m["vgpr_spill_count"] == 0, name
 
 
+@pytest.mark.parametrize("src,pattern", [("q4_gemv.hip", "gemv_bal_kernel"),
+                                         ("q4_gemv_tile.hip", "gemv_tile_kernel")])
+def test_dynamic_lds_kernels_have_no_static_lds(src, pattern):
+    """The decode kernels launch with all 160 KB of a CU's LDS as dynamic
+    shared memory, so any static LDS (for example the reduction buffer behind
+    __syncthreads_or) would make every such launch invalid."""
+    meta = metadata(asm(src))
+    names = [nm for nm in meta if pattern in nm]
+    assert names, pattern
+    for nm in names:
+        assert meta[nm]["group_segment_fixed_size"] == 0, nm
+
+
 @pytest.mark.parametrize("src,pattern", [("q4_gemm.hip", "gemm_mfma_kernel"),
                                          ("q4_gemv.hip", "gemv_bal_kernel"),
                                          ("q4_gemv.hip", "gemv_stream_kernel"),
