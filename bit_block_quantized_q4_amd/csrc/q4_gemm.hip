@@ -43,6 +43,8 @@
 // that finds a non-finite one recomputes its tile (and K range) on the exact
 // route from the original activations.  In-domain results are finite, so the
 // check never fires on them.
+#include <initializer_list>
+
 #include "q4_device.hpp"
 
 namespace q4 {
@@ -970,55 +972,156 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   for (int i = 0; i < 4; ++i) y[r * ldy + c + i] = static_cast<YT>(acc[i]);
 }
 
-// Launch plan: main tiles (256 x 256 with 8 waves for m >= 1024, else
-// 128 x 128 with 4: slice-K when k % 256 == 0 and k >= 1024) over the
-// leading n_main columns in whole rounds of one tile per compute unit.  When
-// a partial round would be left, the remaining columns run with K split
-// `splits` ways so that the tail fills the compute units (slice-K tiles when
-// k allows, else the main tiles); the fp32 partials go to the workspace and
-// one reduction sums them in split order.
+// Launch plan.  Columns [0, n_main) run `main` tiles over all of K in whole
+// rounds of one tile per compute unit; columns [n_main, n) run `tail` tiles
+// with K split `splits` ways (fp32 partials in the workspace, then one
+// reduction in split order).  n_main = 0 splits every tile: a launch with
+// fewer tiles than compute units (k/v projections of a 256-row chunk are 16
+// slice-K tiles) then fills the chip with K splits instead of leaving most of
+// it idle.  The candidates -- 256 x 256 or 128 x 128 main tiles, with or
+// without a split tail, or every tile split -- are compared on a cost model
+// whose constants were measured on MI355X (graph replays, one round of 256
+// tiles, K from 1024 to 10240): a tile costs a fixed ~9.5 us (launch ramp,
+// prologue copies, epilogue) plus per 64-wide k step ~2.05 us (256 x 256) or
+// ~0.50 us (slice-K 128 x 128) with every compute unit busy, about a third
+// less per step with few busy (the matrix cores are power-limited); a split
+// adds its fp32 partial traffic and a reduction launch.
+enum class Tile : int { Big = 0, SliceK = 1, Out128 = 2 };
+
 struct GemmPlan {
-  bool big = false;
-  bool slicek = false;       // 128 x 128 slice-K main tiles (k % 256 == 0)
-  bool tail_slicek = false;  // the split-K tail runs slice-K tiles
+  Tile main = Tile::Out128, tail = Tile::Out128;
   int64_t n_main = 0;
   int splits = 1, kps = 0;
   size_t ws_bytes = 0;
+  double est_us = 0.0;
 };
 
+int tile_rows(Tile t) { return t == Tile::Big ? 256 : 128; }
+
+// Estimated microseconds of one round of `wgs` workgroups of tile type t over
+// `steps` 64-wide k steps on `cu` compute units.
+double round_us(Tile t, int64_t steps, int64_t wgs, int64_t cu) {
+  const double full = t == Tile::Big ? 2.05 : t == Tile::SliceK ? 0.50 : 0.86;
+  const double fill = wgs >= cu ? 1.0 : static_cast<double>(wgs) / static_cast<double>(cu);
+  return 9.5 + static_cast<double>(steps) * full * (0.65 + 0.35 * fill);
+}
+
+// Every tile of columns [c0, n) with K split s ways (s = 1: no split).
+double split_us(Tile t, int64_t m, int64_t nc, int nks, int s, int kps, int64_t cu) {
+  const int64_t bt = tile_rows(t);
+  const int64_t tiles = ((m + bt - 1) / bt) * ((nc + bt - 1) / bt) * s;
+  const int64_t rounds = (tiles + cu - 1) / cu;
+  double us = 0.0;
+  for (int64_t r = 0; r < rounds; ++r) {
+    const int64_t w = r + 1 < rounds ? cu : tiles - r * cu;
+    us += round_us(t, kps, w, cu);
+  }
+  if (s > 1) {
+    const double part = static_cast<double>(s) * static_cast<double>(m * nc) * 4.0;
+    us += 2.0 + 2.0 * part / 8.0e6;  // partials written, then read (mostly last-level cache)
+  }
+  (void)nks;
+  return us;
+}
+
+// Steps per split for s splits of nks steps (whole 4-step segments for slice-K).
+int split_kps(Tile t, int nks, int s) {
+  int kps = (nks + s - 1) / s;
+  if (t == Tile::SliceK) kps = (kps + 3) / 4 * 4;
+  return kps;
+}
+
 GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
-  GemmPlan p;
-  p.big = m >= 1024;
-  const bool sk_ok = k % 256 == 0 && k >= 1024;  // short k: prologue and reduction dominate
-  p.slicek = !p.big && sk_ok;
-  const int bm = p.big ? 256 : 128, bn = p.big ? 256 : 128;
+  GemmPlan best;
   const int64_t cu = device_cu_count();
-  const int64_t tm = (m + bm - 1) / bm, tn = (n + bn - 1) / bn;
   const int nks = static_cast<int>(k / kBK);
-  p.n_main = n;
-  p.kps = nks;
-  if (k % kBK != 0 || tm * tn <= cu || (tm * tn) % cu == 0 || (n % 4) != 0) return p;
-  const int64_t tn_main = (tm * tn / cu) * cu / tm;  // column tiles in whole rounds
-  if (tn_main < 1 || tn_main >= tn) return p;
-  const int64_t nt = n - tn_main * bn;
-  // The tail runs slice-K 128 x 128 tiles when k allows and they still take
-  // at least two K splits: behind 256 x 256 main tiles that is four times the
-  // tiles, so fewer splits (less fp32 partial traffic) fill the compute
-  // units, and its epilogue stores four columns at a time.
-  const int64_t sk_tiles = ((m + 127) / 128) * ((nt + 127) / 128);
-  p.tail_slicek = sk_ok && cu / sk_tiles >= 2;
-  const int tb = p.tail_slicek ? 128 : bm;
-  const int64_t tail_tiles = ((m + tb - 1) / tb) * ((nt + tb - 1) / tb);
-  int64_t splits = cu / tail_tiles;
-  if (splits > nks) splits = nks;
-  if (splits < 2) return p;
-  int kps = static_cast<int>((nks + splits - 1) / splits);
-  if (p.tail_slicek) kps = (kps + 3) / 4 * 4;  // whole 4-step weight segments
-  p.n_main = tn_main * bn;
-  p.kps = kps;
-  p.splits = (nks + kps - 1) / kps;
-  p.ws_bytes = static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(nt) * 4;
-  return p;
+  const bool sk_ok = k % 256 == 0 && k >= 1024;  // short k: prologue and reduction dominate
+  const bool split_ok = k % kBK == 0 && n % 4 == 0;
+  best.main = m >= 1024 ? Tile::Big : sk_ok ? Tile::SliceK : Tile::Out128;
+  best.n_main = n;
+  best.kps = nks;
+  best.est_us = split_us(best.main, m, n, nks, 1, nks, cu);
+  if (k % kBK != 0) return best;
+
+  // 256 x 256 main tiles for m >= 1024 (128 x 128 slice-K tiles there only
+  // when the 256 x 256 tiles would leave compute units idle: at full rounds
+  // the 256 x 256 tile measured a few percent faster than the model says);
+  // 128 x 128 tiles below, slice-K where k allows.
+  const bool big_fills = ((m + 255) / 256) * ((n + 255) / 256) >= cu;
+  std::initializer_list<Tile> mains = {Tile::Big, Tile::SliceK, Tile::Out128};
+  for (Tile mt : mains) {
+    if (mt == Tile::SliceK && (!sk_ok || (m >= 1024 && big_fills))) continue;
+    if (mt == Tile::Out128 && (sk_ok || m >= 1024)) continue;  // slice-K is the faster 128 x 128 tile
+    if (mt == Tile::Big && m < 1024) continue;
+    const int64_t bt = tile_rows(mt);
+    const int64_t tm = (m + bt - 1) / bt, tn = (n + bt - 1) / bt;
+    auto consider = [&](const GemmPlan& c) {
+      if (c.est_us < best.est_us) best = c;
+    };
+    // main tiles over every column, no split
+    {
+      GemmPlan c;
+      c.main = c.tail = mt;
+      c.n_main = n;
+      c.kps = nks;
+      c.est_us = split_us(mt, m, n, nks, 1, nks, cu);
+      consider(c);
+    }
+    if (!split_ok) continue;
+    // every tile split s ways
+    if (tm * tn < cu) {
+      for (int64_t s = 2; s <= cu / (tm * tn) && s <= nks; ++s) {
+        GemmPlan c;
+        c.main = c.tail = mt;
+        c.n_main = 0;
+        c.kps = split_kps(mt, nks, static_cast<int>(s));
+        c.splits = (nks + c.kps - 1) / c.kps;
+        if (c.splits < 2) continue;
+        c.est_us = split_us(mt, m, n, nks, c.splits, c.kps, cu);
+        c.ws_bytes = static_cast<size_t>(c.splits) * static_cast<size_t>(m * n) * 4;
+        consider(c);
+      }
+    }
+    // whole rounds of main tiles, the remaining columns split
+    if (tm * tn > cu && (tm * tn) % cu != 0) {
+      const int64_t tn_main = (tm * tn / cu) * cu / tm;
+      if (tn_main >= 1 && tn_main < tn) {
+        const int64_t nt = n - tn_main * bt;
+        const double main_us = split_us(mt, m, tn_main * bt, nks, 1, nks, cu);
+        for (Tile tt : mains) {
+          if (tt == Tile::SliceK && !sk_ok) continue;
+          if (tt == Tile::Out128 && sk_ok) continue;
+          if (tt == Tile::Big && mt != Tile::Big) continue;
+          const int64_t tb = tile_rows(tt);
+          const int64_t ttiles = ((m + tb - 1) / tb) * ((nt + tb - 1) / tb);
+          for (int64_t s = 2; s <= cu / ttiles && s <= nks; ++s) {
+            GemmPlan c;
+            c.main = mt;
+            c.tail = tt;
+            c.n_main = tn_main * bt;
+            c.kps = split_kps(tt, nks, static_cast<int>(s));
+            c.splits = (nks + c.kps - 1) / c.kps;
+            if (c.splits < 2) continue;
+            c.est_us = main_us + split_us(tt, m, nt, nks, c.splits, c.kps, cu);
+            c.ws_bytes = static_cast<size_t>(c.splits) * static_cast<size_t>(m * nt) * 4;
+            consider(c);
+          }
+        }
+      }
+    }
+  }
+  return best;
+}
+
+template <typename YT>
+hipError_t launch_tile_type(Tile t, const half_t* x, const uint8_t* packed, int64_t c0, int64_t nc,
+                            YT* yc, int64_t m, int64_t k, int64_t ldy, int splits, int kps,
+                            int64_t zstride, XSrc xe, hipStream_t s) {
+  if (t == Tile::Big)
+    return launch_tiled<256, 256, 2, 4, YT>(x, packed, c0, nc, yc, m, k, ldy, splits, kps, zstride, xe, s);
+  if (t == Tile::SliceK)
+    return launch_slicek<YT>(x, packed, c0, nc, yc, m, k, ldy, splits, kps, zstride, xe, s);
+  return launch_tiled<128, 128, 2, 2, YT>(x, packed, c0, nc, yc, m, k, ldy, splits, kps, zstride, xe, s);
 }
 
 template <typename YT>
@@ -1026,19 +1129,16 @@ hipError_t dispatch_tiled(const half_t* x, const uint8_t* packed, YT* y, int64_t
                           int64_t k, void* workspace, XSrc xe, hipStream_t s) {
   const GemmPlan p = gemm_plan(m, n, k);
   const int nks = static_cast<int>(k / kBK);
-  hipError_t e = p.big      ? launch_tiled<256, 256, 2, 4, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, xe, s)
-                 : p.slicek ? launch_slicek<YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, xe, s)
-                            : launch_tiled<128, 128, 2, 2, YT>(x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, xe, s);
-  if (e != hipSuccess || p.n_main == n) return e;
-  // Tail: split z of K writes part[z], m x nt with row stride nt.
+  hipError_t e = hipSuccess;
+  if (p.n_main > 0) {
+    e = launch_tile_type<YT>(p.main, x, packed, 0, p.n_main, y, m, k, n, 1, nks, 0, xe, s);
+    if (e != hipSuccess || p.n_main == n) return e;
+  }
+  // Split columns: split z of K writes part[z], m x nt with row stride nt.
   const int64_t nt = n - p.n_main;
   float* part = static_cast<float*>(workspace);
-  e = p.tail_slicek ? launch_slicek<float>(x, packed, p.n_main, nt, part, m, k, nt, p.splits,
-                                            p.kps, m * nt, xe, s)
-      : p.big        ? launch_tiled<256, 256, 2, 4, float>(x, packed, p.n_main, nt, part, m, k, nt,
-                                                          p.splits, p.kps, m * nt, xe, s)
-                     : launch_tiled<128, 128, 2, 2, float>(x, packed, p.n_main, nt, part, m, k, nt,
-                                                          p.splits, p.kps, m * nt, xe, s);
+  e = launch_tile_type<float>(p.tail, x, packed, p.n_main, nt, part, m, k, nt, p.splits, p.kps,
+                              m * nt, xe, s);
   if (e != hipSuccess) return e;
   const int64_t quads = m * nt / 4;
   YT* yt = y + p.n_main;

@@ -379,3 +379,34 @@ def test_bf16_activations_beyond_the_fp16_range(q4lib, gpu, m, n, k):
                               n=n, k=k))
     assert np.isfinite(y).all()
     assert_matmul_close(y, oracle.widen_bf16(xb), packed, n, k, what=f"bf16 range m{m} n{n} k{k}")
+
+
+# Launches with fewer tiles than compute units, split along K on every tile:
+# slice-K tiles (the 256-row chunk's k/v and down projections, a 64-row and a
+# one-row prompt), 256 x 256 tiles (m >= 1024, k % 256 != 0), output-split
+# 128 x 128 tiles (k % 256 != 0, down to one 64-wide k step per split);
+# slice-K main tiles plus a split tail at m >= 1024 where 256 x 256 tiles
+# would under-fill the chip; one round of slice-K tiles at m = 4096.
+SPLIT_EVERY_TILE = [(256, 1024, 5120), (256, 5120, 17408), (64, 768, 2048), (1, 1024, 5120),
+                    (1100, 1024, 1088), (2048, 520, 4160), (200, 512, 4160), (100, 300, 1600),
+                    (1500, 3000, 1024), (4096, 1024, 5120)]
+
+
+@pytest.mark.parametrize("m,n,k", SPLIT_EVERY_TILE)
+def test_split_every_tile(q4lib, gpu, m, n, k):
+    """Every output against the oracle (fp16 and fp32 output), the workspace
+    the plan needs, and bit-identical results on a second run."""
+    import torch
+    w = synth.random_weights(197 * m + n + k, n, k, "student_t")
+    x = synth.random_activations(199 * m + k, m, k, "f16")
+    packed = oracle.quantize(w)
+    xd, pd = to_dev(x, gpu), to_dev(packed, gpu)
+    need = q4lib.q4_gemm_workspace_size(m, n, k)
+    if (m, n, k) != (4096, 1024, 5120):
+        assert need > 0, "expected a split plan"
+    for ydt in (torch.float32, torch.float16):
+        a = q4lib.q4_gemm(xd, pd, y_dtype=ydt, n=n, k=k)
+        b = q4lib.q4_gemm(xd, pd, y_dtype=ydt, n=n, k=k)
+        assert torch.equal(a.view(torch.int16 if ydt == torch.float16 else torch.int32),
+                           b.view(torch.int16 if ydt == torch.float16 else torch.int32))
+        assert_matmul_close(to_host(a), x, packed, n, k, what=f"split m{m} n{n} k{k} {ydt}")
