@@ -1,34 +1,38 @@
 #!/usr/bin/env python3
 """Q4_0 linear-layer benchmark on one MI355X.
 
-Headline: batched-decode GEMV weight GB/s on the 5120 x 5120 attention
-projection (M = 1, 4, 10, 16 per step, fp16 activations, fp16 output), with
-the packed weights rotated over >= 1 GiB of distinct copies so every launch
-streams from HBM rather than the 256 MB last-level cache.  One step = one
-GEMV launch per batch size, each on its own weight copy.  The W warm-up steps
-and the K timed steps are each recorded into a HIP graph and replayed, so the
-HIP events around the replay time GPU work, not Python's launch latency.
+Headline: one 27B-class dense decoder layer's linears (q/k/v, o, gate/up,
+down; K = 5120 or 17408; Student-t(3) x 0.02 weights, fp16 activations, fp16
+outputs) in batched decode at M = 1 and M = 10.  q/k/v and gate/up each run as
+one launch over their packed rows stacked, so a step is eight q4_gemv launches
+(four per batch size) streaming 2 x 185.8 MB of packed weights; layer copies
+are rotated over >= 1 GiB so every launch reads HBM rather than the 256 MB
+last-level cache.  `value` is the step's packed-weight GB/s; `roofline` is the
+step's dominant launch (algorithmic bytes: packed weights + x + y) against
+8 TB/s.  The W warm-up steps and the K timed steps are recorded into HIP
+graphs and replayed, so the HIP events around a replay time GPU work, not
+Python's launch latency.
+
+The GEMM half (`gemm`): the same layer's prefill at M = 4096 (four launches),
+TFLOP/s against the fp16 matrix-core peak, with its own roofline object on the
+dominant launch and the shader clock sampled during the leg.
 
 The same JSON line carries:
-  roofline      -- the step's dominant GEMV launch (K launches of that batch
-                   size back to back): algorithmic bytes (packed weights + x +
-                   y) / mean launch time, against 8 TB/s HBM; `traffic` is the
-                   HBM bytes per launch from the committed counter passes;
-  gemm          -- prefill GEMM on the 2048 x 17408 x 5120 workload, whole
-                   batch and 8 chunks of 256 rows, TFLOP/s against fp16 MFMA,
-                   plus the chunk-size sweep (128, 256 and 512 rows);
-  quantize      -- the quantiser on the same 5120 x 5120 fp32 weight;
-  layer_decode  -- one 27B-class layer's seven decode linears at M = 1 and 10,
-                   as seven launches and as four (q/k/v and gate/up each one
-                   launch on their concatenated packed rows);
-  layer_prefill -- the same layer's GEMMs at M = 256 and 4096, seven launches
-                   and four;
-  other_configs -- the 512 x 512 fp32 linear (latency: quantise, GEMV) and the
-                   17408 x 5120 gate/up weight with outlier blocks, m = 1, 10, 32;
-  bf16          -- bf16 activations on the headline GEMV and the prefill GEMM;
-  host_twin     -- the host-CPU twin (libq4host) on the same packed bytes,
-                   on the host cores (a second backend, not a GPU figure);
-  cpu_baseline  -- the CPU oracle timed on a bounded sample of the step.
+  read_floor     -- a plain library read (torch's sum) of the same rotated
+                    packed buffers, launch by launch: what streaming these bytes
+                    costs without any Q4_0 work;
+  layer_decode   -- the layer as seven launches against four, M = 1 and 10;
+  layer_prefill  -- the layer's GEMMs at M = 256 and 4096, seven and four;
+  attn_proj      -- the 5120 x 5120 projection at M = 1, 4, 10, 16;
+  gemm           -- also the 2048 x 17408 x 5120 prefill, whole and as 8 chunks
+                    of 256 rows, and the chunk-size sweep (128, 256, 512);
+  quantize       -- the quantiser on the 5120 x 5120 fp32 weight;
+  other_configs  -- the 512 x 512 fp32 linear (latency) and the 17408 x 5120
+                    weight with outlier blocks, m = 1, 10, 32;
+  bf16           -- bf16 activations on the attention projection and prefill;
+  host_twin      -- the host-CPU twin (libq4host) on the same packed bytes;
+  cpu_baseline   -- the CPU oracle per configuration (quantise + matmul) on
+                    bounded samples, on the host cores of this process.
 
 Counter passes (HBM traffic): run `bench.py --traffic` once under
 `rocprofv3 --pmc FETCH_SIZE` and once under `--pmc WRITE_SIZE`, then
@@ -193,36 +197,6 @@ def bench_gemv(q4, torch, dev, steps, warmup, rotate_bytes):
     }
 
 
-def bench_gemv_dense_library(torch, dev, s, per_m, steps, rotate_bytes):
-    """Context, not the metric: the same decode products through the fp16
-    library GEMM (torch.mm) on the unquantised weights rounded to fp16, as a
-    contiguous [k, n] operand, rotated over >= rotate_bytes like the packed
-    copies; and the Q4_0 launches' speed relative to it."""
-    n, k, ms = s["n"], s["k"], s["ms"]
-    wt0 = torch.from_numpy(s["w_host"]).to(dev).half().t().contiguous()
-    dbytes = n * k * 2
-    copies = max(4, -(-rotate_bytes // dbytes))
-    wts = [wt0] + [wt0.clone() for _ in range(copies - 1)]
-    q4_us = {r["m"]: r["mean_us"] for r in per_m}
-    rows = []
-    for m in ms:
-        x, y = s["x"][:m], s["ys"][m]
-
-        def fn():
-            for i in range(steps):
-                torch.mm(x, wts[i % copies], out=y)
-        g = capture(torch, fn)
-        g.replay()
-        avg_s = replay_seconds(torch, g) / steps
-        del g
-        rows.append({"m": m, "mean_us": avg_s * 1e6, "weight_gbs": dbytes / avg_s / 1e9,
-                     "q4_speed_vs_library": avg_s * 1e6 / q4_us[m]})
-    del wts, wt0
-    torch.cuda.empty_cache()
-    return {"op": "torch.mm, fp16 x and fp16 weights [k, n] contiguous", "weight_bytes": dbytes,
-            "copies_rotated": copies, "per_m": rows}
-
-
 def bench_quantize(q4, torch, dev, w_host, reps, rotate_bytes):
     n, k = w_host.shape
     in_bytes = n * k * 4
@@ -245,11 +219,8 @@ def bench_quantize(q4, torch, dev, w_host, reps, rotate_bytes):
                          "traffic": load_traffic("quantize_fp32_5120x5120")}}
 
 
-def gemm_setup(q4, torch, dev, x_dtype=None, dense=False):
-    """The prefill workload's launches.  With dense=True also returns
-    dense(cs): the same product in cs-row launches of the fp16 library GEMM
-    (torch.mm) on the unquantised weights rounded to fp16, a same-box
-    reference for the matrix-core kernels."""
+def gemm_setup(q4, torch, dev, x_dtype=None):
+    """The 2048-row prefill workload's launches: whole() and chunked(cs)."""
     import synth
     wl = synth.WORKLOADS[4]
     lin = wl.linears[0]
@@ -257,7 +228,6 @@ def gemm_setup(q4, torch, dev, x_dtype=None, dense=False):
     w = synth.workload_weights(wl, lin)
     wd = torch.from_numpy(w).to(dev)
     packed = q4.q4_quantize(wd)
-    wt = wd.half().t().contiguous() if dense else None  # [k, n] fp16, contiguous
     del w, wd
     x = torch.from_numpy(synth.workload_activations(wl, k, m)).to(dev)
     if x_dtype is not None:
@@ -276,16 +246,7 @@ def gemm_setup(q4, torch, dev, x_dtype=None, dense=False):
                 q4.q4_gemm(x[c * cs:(c + 1) * cs], packed, y=y[c * cs:(c + 1) * cs], workspace=work)
         return fn
 
-    if not dense:
-        return m, n, k, whole, chunked
-
-    def dense_chunked(cs):
-        def fn():
-            for c in range(m // cs):
-                torch.mm(x[c * cs:(c + 1) * cs], wt, out=y[c * cs:(c + 1) * cs])
-        return fn
-
-    return m, n, k, whole, chunked, dense_chunked
+    return m, n, k, whole, chunked
 
 
 def time_gemm_calls(torch, fn, reps):
@@ -306,7 +267,7 @@ def bench_gemm(q4, torch, dev, reps):
     smaller chunks bound the activation memory a step holds, at the cost of
     streaming the packed weight once per chunk and of fewer output tiles per
     launch."""
-    m, n, k, whole, chunked, dense = gemm_setup(q4, torch, dev, dense=True)
+    m, n, k, whole, chunked = gemm_setup(q4, torch, dev)
     flop = 2.0 * m * n * k
     res = {}
     for name, fn, calls in (("whole_2048", whole, 1), ("chunked_8x256", chunked(256), 8)):
@@ -314,14 +275,6 @@ def bench_gemm(q4, torch, dev, reps):
         tf = flop / avg_s / 1e12
         res[name] = {"mean_us": avg_s * 1e6, "launches": calls, "tflops": tf,
                      "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS}
-    # the fp16 library GEMM of the same shapes on the same box (context, not
-    # the metric): speed of the Q4_0 launches relative to it
-    lib = {}
-    for name, cs in (("whole_2048", m), ("chunked_8x256", 256)):
-        avg_s = time_gemm_calls(torch, dense(cs), reps)
-        lib[name] = {"mean_us": avg_s * 1e6, "frac_mfma": flop / avg_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                     "q4_speed_vs_library": avg_s * 1e6 / res[name]["mean_us"]}
-    res["dense_fp16_library"] = {"op": "torch.mm, fp16 x and fp16 weights [k, n] contiguous", **lib}
     sweep = []
     for cs in CHUNK_ROWS:
         avg_s = time_gemm_calls(torch, chunked(cs), reps)
@@ -329,70 +282,327 @@ def bench_gemm(q4, torch, dev, reps):
         sweep.append({"chunk_rows": cs, "launches": m // cs, "mean_us": avg_s * 1e6,
                       "us_per_chunk": avg_s * 1e6 / (m // cs), "tflops": tf,
                       "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS})
-    best = res["whole_2048"]["tflops"]
-    return {
-        "workload": "prefill_chunked_2048x17408x5120", "m": m, "n": n, "k": k,
-        **res, "chunk_sweep": sweep,
-        "roofline": {"bound": "mfma", "achieved": best, "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": best / MFMA_F16_PEAK_TFLOPS,
-                     "traffic": load_traffic("gemm_2048x17408x5120"),
-                     "mfma_util_pct": load_mfma_util("gemm_mfma_256x256_f16_out")},
-    }
+    return {"workload": "prefill_chunked_2048x17408x5120", "m": m, "n": n, "k": k,
+            **res, "chunk_sweep": sweep}
 
 
-def bench_layer_decode(q4, torch, dev, steps, rotate_bytes, ms=(1, 10)):
-    """Decode through one 27B-class layer's seven linears (q, k, v, o, gate,
-    up, down) at M = 1 and 10: seven launches, against four where q/k/v and
-    gate/up run as one launch each on their packed rows concatenated (packed
-    rows are independent, so a concatenated buffer is simply a taller weight).
-    Each linear's packed copy is a row slice of its group's buffer, so both
-    variants stream the same bytes; layer copies are rotated over >= 1 GiB."""
+# ------------------------------------------------------------ the 27B-class layer
+
+LAYER_GROUPS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")),
+                ("down", ("down",)))
+
+
+def layer_linears():
     import synth
-    lins = {l.name: l for l in synth.WORKLOADS[5].linears}
-    k_model = lins["q"].k
-    groups = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gateup", ["gate", "up"]), ("down", ["down"])]
-    layer_bytes = sum(l.n * (l.k // QK) * BLOCK_BYTES for l in lins.values())
-    copies = max(2, -(-rotate_bytes // layer_bytes))
+    return {l.name: l for l in synth.WORKLOADS[5].linears}
+
+
+def packed_bytes(rows, k):
+    return rows * (k // QK) * BLOCK_BYTES
+
+
+def student_t_device(torch, shape, gen, dev, sigma=0.02):
+    """Student-t(3) x sigma drawn on the device from its definition:
+    Z / sqrt((Z1^2 + Z2^2 + Z3^2) / 3) with independent standard normals."""
+    z = torch.randn(shape, device=dev, generator=gen)
+    v = torch.zeros(shape, device=dev)
+    for _ in range(3):
+        e = torch.randn(shape, device=dev, generator=gen)
+        v.addcmul_(e, e)
+        del e
+    return z.div_(v.div_(3.0).sqrt_()).mul_(sigma)
+
+
+def layer_setup(q4, torch, dev, seed=5):
+    """One layer's packed weights as the four launch groups: each group one
+    buffer, each linear quantised into its row slice (Student-t(3) x 0.02)."""
+    lins = layer_linears()
     gen = torch.Generator(device=dev)
-    gen.manual_seed(5)
-    layers = []
-    for _ in range(copies):
-        bufs, views = {}, {}
-        for gname, names in groups:
-            kk = lins[names[0]].k
-            rows = sum(lins[nm].n for nm in names)
-            buf = torch.empty((rows, (kk // QK) * BLOCK_BYTES), dtype=torch.uint8, device=dev)
-            r = 0
-            for nm in names:
-                n = lins[nm].n
-                w = torch.randn((n, kk), device=dev, generator=gen) * 0.02
-                views[nm] = buf[r:r + n]
-                q4.q4_quantize(w, packed=views[nm])
-                r += n
-            bufs[gname] = buf
-        layers.append((bufs, views))
+    gen.manual_seed(seed)
+    bufs, views = {}, {}
+    for g, names in LAYER_GROUPS:
+        kk = lins[names[0]].k
+        rows = sum(lins[nm].n for nm in names)
+        buf = torch.empty((rows, (kk // QK) * BLOCK_BYTES), dtype=torch.uint8, device=dev)
+        r = 0
+        for nm in names:
+            nn = lins[nm].n
+            views[nm] = buf[r:r + nn]
+            q4.q4_quantize(student_t_device(torch, (nn, kk), gen, dev), packed=views[nm])
+            r += nn
+        bufs[g] = buf
     torch.cuda.synchronize()
+    return lins, bufs, views
+
+
+def group_shape(lins, g):
+    names = dict(LAYER_GROUPS)[g]
+    return sum(lins[nm].n for nm in names), lins[names[0]].k
+
+
+def rotated(torch, buf, rotate_bytes, minimum=2):
+    """Distinct copies of buf totalling >= rotate_bytes (buf first)."""
+    nb = buf.numel() * buf.element_size()
+    count = max(minimum, -(-rotate_bytes // nb))
+    return [buf] + [buf.clone() for _ in range(count - 1)]
+
+
+def bench_headline_decode(q4, torch, dev, steps, warmup, rotate_bytes, ms=(1, 10)):
+    """The headline step: the layer's four decode launches at each M in ms,
+    layer copies rotated; then each launch on its own, K launches back to back
+    over >= rotate_bytes of copies of its group buffer (so no launch finds its
+    weights in the last-level cache)."""
+    lins, bufs, _ = layer_setup(q4, torch, dev)
+    layer_bytes = sum(packed_bytes(*group_shape(lins, g)) for g, _ in LAYER_GROUPS)
+    ncopies = max(2, -(-rotate_bytes // layer_bytes))
+    layers = [bufs] + [{g: b.clone() for g, b in bufs.items()} for _ in range(ncopies - 1)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    xs = {m: torch.randn((m, lins["q"].k), device=dev, generator=gen).half() for m in ms}
+    xd = {m: torch.randn((m, lins["down"].k), device=dev, generator=gen).half() for m in ms}
+    ys = {(m, g): torch.empty((m, group_shape(lins, g)[0]), dtype=torch.float16, device=dev)
+          for m in ms for g, _ in LAYER_GROUPS}
+
+    def launch(m, g, buf):
+        q4.q4_gemv(xd[m] if g == "down" else xs[m], buf, y=ys[(m, g)])
+
+    def step_fn(nsteps, first):
+        def fn():
+            i = first
+            for _ in range(nsteps):
+                for m in ms:  # every batch size reads the next layer copy
+                    lay = layers[i % ncopies]
+                    for g, _ in LAYER_GROUPS:
+                        launch(m, g, lay[g])
+                    i += 1
+        return fn
+
+    gw = capture(torch, step_fn(max(warmup, 1), 0))
+    gt = capture(torch, step_fn(steps, max(warmup, 1) * len(ms)))
+    gw.replay()
+    step_s = replay_seconds(torch, gt) / steps
+    del gw, gt, layers
+    per_launch = []
+    for g, _ in LAYER_GROUPS:
+        rows, k = group_shape(lins, g)
+        copies = rotated(torch, bufs[g], rotate_bytes)
+        for m in ms:
+            def fn(m=m, g=g, copies=copies):
+                for i in range(steps):
+                    launch(m, g, copies[i % len(copies)])
+            gr = capture(torch, fn)
+            gr.replay()
+            t = replay_seconds(torch, gr) / steps
+            del gr
+            wb = packed_bytes(rows, k)
+            alg = wb + 2 * m * k + 2 * m * rows
+            per_launch.append({"group": g, "m": m, "n": rows, "k": k, "mean_us": t * 1e6,
+                               "weight_bytes": wb, "alg_bytes": alg,
+                               "weight_gbs": wb / t / 1e9, "alg_gbs": alg / t / 1e9,
+                               "frac_hbm": alg / t / 1e9 / HBM_PEAK_GBS,
+                               "copies_rotated": len(copies)})
+        del copies
+    return {"lins": lins, "bufs": bufs, "layer_bytes": layer_bytes, "ncopies": ncopies,
+            "ms": list(ms), "step_s": step_s,
+            "value_gbs": layer_bytes * len(ms) / step_s / 1e9, "per_launch": per_launch}
+
+
+def floor_lib():
+    """libq4floor.so (the plain-read kernel, include/q4_read_floor.h)."""
+    import ctypes
+    import torch  # noqa: F401  (its HIP runtime first, as for libq4)
+    L = ctypes.CDLL(str(ROOT / "bit_block_quantized_q4_amd" / "libq4floor.so"))
+    L.q4_read_floor.restype = ctypes.c_int
+    L.q4_read_floor.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                ctypes.c_void_p]
+    return L
+
+
+FLOOR_GRIDS = (256, 512, 1024, 2048, 4096)
+
+
+def bench_read_floor(torch, bufs, rotate_bytes, reps):
+    """A plain read of the same bytes: libq4floor's streaming kernel over each
+    group's packed buffer, >= rotate_bytes of rotated copies as the GEMV reads
+    them, at several grid sizes (the best is reported).  It does no Q4_0
+    work, so it shows what streaming these bytes in one launch costs here."""
+    L = floor_lib()
+    out = {}
+    for g, buf in bufs.items():
+        copies = rotated(torch, buf, rotate_bytes)
+        nb = buf.numel()
+        sink = torch.empty(max(FLOOR_GRIDS) * 256, dtype=torch.int32, device=buf.device)
+        best = None
+        for wg in FLOOR_GRIDS:
+            def fn(wg=wg):
+                st = torch.cuda.current_stream().cuda_stream
+                for i in range(reps):
+                    rc = L.q4_read_floor(copies[i % len(copies)].data_ptr(), nb, sink.data_ptr(), wg, st)
+                    if rc != 0:
+                        raise RuntimeError(f"q4_read_floor returned {rc}")
+            gr = capture(torch, fn)
+            gr.replay()
+            t = replay_seconds(torch, gr) / reps
+            del gr
+            if best is None or t < best[0]:
+                best = (t, wg)
+        del copies, sink
+        t, wg = best
+        out[g] = {"bytes": nb, "mean_us": t * 1e6, "gbs": nb / t / 1e9,
+                  "frac_hbm": nb / t / 1e9 / HBM_PEAK_GBS, "workgroups": wg}
+    return out
+
+
+class ClockSampler:
+    """Samples the GPU's shader clock (amdsmi, MHz) on a host thread while a
+    leg runs; reports None where amdsmi cannot read it."""
+
+    def __init__(self, period_s=0.005):
+        self.period, self.samples, self.error = period_s, [], None
+        self._stop, self._thread, self._h = None, None, None
+
+    def __enter__(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read = lambda: amdsmi.amdsmi_get_clock_info(self._h, amdsmi.AmdSmiClkType.GFX)["clk"]
+            self._read()
+        except Exception as e:  # noqa: BLE001 - any failure leaves the clock unreported
+            self.error = f"{type(e).__name__}: {e}"[:200]
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(float(self._read()))
+                except Exception:  # noqa: BLE001
+                    pass
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        try:
+            import amdsmi
+            amdsmi.amdsmi_shut_down()
+        except Exception:  # noqa: BLE001
+            pass
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return {"sclk_mhz": None, "error": self.error or "no samples"}
+        v = np.array(self.samples)
+        return {"sclk_mhz_median": float(np.median(v)), "sclk_mhz_min": float(v.min()),
+                "sclk_mhz_max": float(v.max()), "samples": int(v.size), "peak_sclk_mhz": 2400.0}
+
+
+def bench_headline_prefill(q4, torch, dev, lins, bufs, reps, m=4096):
+    """The layer's prefill at M = m: the four launches as a step, and each on
+    its own (one weight copy: the GEMM is bound by the matrix cores), with
+    the shader clock sampled meanwhile."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(8)
+    x = torch.randn((m, lins["q"].k), device=dev, generator=gen).half()
+    xd = torch.randn((m, lins["down"].k), device=dev, generator=gen).half()
+    ys = {g: torch.empty((m, group_shape(lins, g)[0]), dtype=torch.float16, device=dev)
+          for g, _ in LAYER_GROUPS}
+    wsz = max([q4.q4_gemm_workspace_size(m, *group_shape(lins, g)) for g, _ in LAYER_GROUPS] + [1])
+    work = torch.empty(wsz, dtype=torch.uint8, device=dev)
+
+    def launch(g):
+        q4.q4_gemm(xd if g == "down" else x, bufs[g], y=ys[g], workspace=work)
+
+    def step():
+        for g, _ in LAYER_GROUPS:
+            launch(g)
+
+    flop_step = sum(2.0 * m * group_shape(lins, g)[0] * group_shape(lins, g)[1] for g, _ in LAYER_GROUPS)
+    t_step = time_gemm_calls(torch, step, reps)
+    per_launch = []
+    for g, _ in LAYER_GROUPS:
+        rows, k = group_shape(lins, g)
+        t = time_gemm_calls(torch, lambda g=g: launch(g), reps)
+        fl = 2.0 * m * rows * k
+        per_launch.append({"group": g, "m": m, "n": rows, "k": k, "mean_us": t * 1e6,
+                           "flop": fl, "tflops": fl / t / 1e12,
+                           "frac_mfma": fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS})
+    # The shader clock under this load: the step replayed back to back for
+    # about a second while a host thread samples it.
+    gsoak = capture(torch, step)
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 1.0:
+            for _ in range(20):
+                gsoak.replay()
+            torch.cuda.synchronize()
+    del gsoak
+    tf = flop_step / t_step / 1e12
+    dom = max(per_launch, key=lambda r: r["mean_us"])
+    return {"workload": f"layer_27b_dense prefill, M = {m}, 4 launches (q/k/v and gate/up fused)",
+            "m": m, "us_per_layer": t_step * 1e6, "tflops": tf, "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS,
+            "per_launch": per_launch, "clock": clk.summary(),
+            "roofline": {"bound": "mfma", "achieved": dom["tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": dom["frac_mfma"],
+                         "traffic": load_traffic(f"gemm_layer_{dom['group']}_m{m}"),
+                         "kernel": f"q4_gemm {dom['group']} {m}x{dom['n']}x{dom['k']}",
+                         "mean_us": dom["mean_us"], "alg_flop_per_launch": dom["flop"],
+                         "mfma_util_pct": load_mfma_util(f"gemm_layer_{dom['group']}_m{m}")}}
+
+
+def group_views(lins, bufs):
+    """Each linear's packed rows as a row slice of its group's buffer."""
+    views = {}
+    for g, names in LAYER_GROUPS:
+        r = 0
+        for nm in names:
+            views[nm] = bufs[g][r:r + lins[nm].n]
+            r += lins[nm].n
+    return views
+
+
+def bench_layer_decode(q4, torch, dev, lins, bufs, steps, rotate_bytes, ms=(1, 10)):
+    """Decode through the layer's seven linears (q, k, v, o, gate, up, down)
+    at M = 1 and 10: seven launches, against four where q/k/v and gate/up run
+    as one launch each on their packed rows concatenated (packed rows are
+    independent, so a concatenated buffer is simply a taller weight).  Each
+    linear's packed copy is a row slice of its group's buffer, so both variants
+    stream the same bytes; layer copies are rotated over >= 1 GiB."""
+    layer_bytes = sum(packed_bytes(*group_shape(lins, g)) for g, _ in LAYER_GROUPS)
+    copies = max(2, -(-rotate_bytes // layer_bytes))
+    layers = [bufs] + [{g: b.clone() for g, b in bufs.items()} for _ in range(copies - 1)]
+    lviews = [group_views(lins, lay) for lay in layers]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
     res = {}
     for m in ms:
-        x = torch.randn((m, k_model), device=dev, generator=gen).half()
+        x = torch.randn((m, lins["q"].k), device=dev, generator=gen).half()
         xd = torch.randn((m, lins["down"].k), device=dev, generator=gen).half()
         ysep = {nm: torch.empty((m, l.n), dtype=torch.float16, device=dev) for nm, l in lins.items()}
-        ygrp = {g: torch.empty((m, sum(lins[nm].n for nm in names)), dtype=torch.float16, device=dev)
-                for g, names in groups}
+        ygrp = {g: torch.empty((m, group_shape(lins, g)[0]), dtype=torch.float16, device=dev)
+                for g, _ in LAYER_GROUPS}
 
         def separate():
             for i in range(steps):
-                _, views = layers[i % copies]
+                views = lviews[i % copies]
                 for nm in ("q", "k", "v", "o", "gate", "up"):
                     q4.q4_gemv(x, views[nm], y=ysep[nm])
                 q4.q4_gemv(xd, views["down"], y=ysep["down"])
 
         def fused():
             for i in range(steps):
-                bufs, _ = layers[i % copies]
+                lay = layers[i % copies]
                 for g in ("qkv", "o", "gateup"):
-                    q4.q4_gemv(x, bufs[g], y=ygrp[g])
-                q4.q4_gemv(xd, bufs["down"], y=ygrp["down"])
+                    q4.q4_gemv(x, lay[g], y=ygrp[g])
+                q4.q4_gemv(xd, lay["down"], y=ygrp["down"])
 
         row = {}
         for name, fn, launches in (("separate", separate, 7), ("fused", fused, 4)):
@@ -408,38 +618,23 @@ def bench_layer_decode(q4, torch, dev, steps, rotate_bytes, ms=(1, 10)):
             "layer_copies_rotated": copies, **res}
 
 
-def bench_layer_prefill(q4, torch, dev, reps, ms=(256, 4096)):
-    """Prefill through one 27B-class layer's seven linears at M = 256 (one
-    chunk) and 4096 rows: seven launches, and four with q/k/v and gate/up
-    each run on their concatenated packed rows.  The GEMM is bound by the
-    matrix cores, so one copy of the layer's weights serves every call."""
-    import synth
-    lins = {l.name: l for l in synth.WORKLOADS[5].linears}
-    groups = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gateup", ["gate", "up"]), ("down", ["down"])]
+def bench_layer_prefill(q4, torch, dev, lins, bufs, reps, ms=(256, 4096)):
+    """Prefill through the layer's seven linears at M = 256 (one chunk) and
+    4096 rows: seven launches, and four with q/k/v and gate/up each run on
+    their concatenated packed rows.  The GEMM is bound by the matrix cores,
+    so one copy of the layer's weights serves every call."""
+    views = group_views(lins, bufs)
     gen = torch.Generator(device=dev)
     gen.manual_seed(6)
-    bufs, views = {}, {}
-    for gname, names in groups:
-        kk = lins[names[0]].k
-        rows = sum(lins[nm].n for nm in names)
-        buf = torch.empty((rows, (kk // QK) * BLOCK_BYTES), dtype=torch.uint8, device=dev)
-        r = 0
-        for nm in names:
-            nn = lins[nm].n
-            views[nm] = buf[r:r + nn]
-            q4.q4_quantize(torch.randn((nn, kk), device=dev, generator=gen) * 0.02, packed=views[nm])
-            r += nn
-        bufs[gname] = buf
     flop_per_row = 2.0 * sum(l.n * l.k for l in lins.values())
     res = {}
     for m in ms:
         x = torch.randn((m, lins["q"].k), device=dev, generator=gen).half()
         xd = torch.randn((m, lins["down"].k), device=dev, generator=gen).half()
         ysep = {nm: torch.empty((m, l.n), dtype=torch.float16, device=dev) for nm, l in lins.items()}
-        ygrp = {g: torch.empty((m, sum(lins[nm].n for nm in names)), dtype=torch.float16, device=dev)
-                for g, names in groups}
-        wsz = max([q4.q4_gemm_workspace_size(m, b.shape[0], lins[names[0]].k)
-                   for (g, names), b in zip(groups, bufs.values())] +
+        ygrp = {g: torch.empty((m, group_shape(lins, g)[0]), dtype=torch.float16, device=dev)
+                for g, _ in LAYER_GROUPS}
+        wsz = max([q4.q4_gemm_workspace_size(m, *group_shape(lins, g)) for g, _ in LAYER_GROUPS] +
                   [q4.q4_gemm_workspace_size(m, l.n, l.k) for l in lins.values()] + [1])
         work = torch.empty(wsz, dtype=torch.uint8, device=dev)
 
@@ -591,79 +786,170 @@ def bench_other_configs(q4, torch, dev, steps, rotate_bytes):
 TRAFFIC_CALIB_BYTES = 512 << 20
 
 
-def traffic_run(q4, torch, dev, rotate_bytes, launches=20):
-    """The launches the two counter passes (FETCH_SIZE, then WRITE_SIZE) read:
-    a plain device copy of known size (torch's negation kernel: reads and writes
-    TRAFFIC_CALIB_BYTES once), then the GEMV at every batch size, the
-    quantiser and the whole-batch GEMM, each repeated."""
+SEPARATOR = "bitwise_not"  # the torch kernel launched between counted launch groups
+ATTN_MS = (1, 4, 10, 16)
+DECODE_MS = (1, 10)
+
+
+def traffic_keys():
+    """The launch groups of traffic_run, in launch order."""
+    keys = ["calib_copy"]
+    keys += [f"gemv_layer_{g}_m{m}" for g, _ in LAYER_GROUPS for m in DECODE_MS]
+    keys += [f"gemv_5120x5120_m{m}" for m in ATTN_MS]
+    keys += ["quantize_fp32_5120x5120"]
+    keys += [f"gemm_layer_{g}_m4096" for g, _ in LAYER_GROUPS]
+    keys += ["gemm_2048x17408x5120"]
+    return keys
+
+
+TRAFFIC_LAUNCHES = {"gemv": 20, "quantize": 20, "gemm": 3, "calib": 3}
+
+
+def launches_of(key):
+    return TRAFFIC_LAUNCHES[key.split("_")[0]]
+
+
+def separator(torch, dev):
+    a = torch.zeros(64, dtype=torch.int8, device=dev)
+    b = torch.empty_like(a)
+    return lambda: torch.bitwise_not(a, out=b)
+
+
+def traffic_run(q4, torch, dev, rotate_bytes):
+    """The launches the counter passes (FETCH_SIZE, WRITE_SIZE, SQ) read, in
+    the order of traffic_keys(), a separator kernel after each group: a plain
+    device copy of known size (torch's negation kernel: reads and writes
+    TRAFFIC_CALIB_BYTES once); the headline layer's decode launches (rotated
+    copies, as timed); the 5120 x 5120 GEMV at each batch size; the quantiser;
+    the layer's prefill launches at M = 4096; the 2048-row prefill."""
+    sep = separator(torch, dev)
     src = torch.ones(TRAFFIC_CALIB_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for _ in range(3):
+    for _ in range(launches_of("calib")):
         torch.neg(src, out=dst)
+    sep()
     del src, dst
+    lins, bufs, _ = layer_setup(q4, torch, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    for g, _ in LAYER_GROUPS:
+        rows, k = group_shape(lins, g)
+        copies = rotated(torch, bufs[g], rotate_bytes)
+        for m in DECODE_MS:
+            x = torch.randn((m, k), device=dev, generator=gen).half()
+            y = torch.empty((m, rows), dtype=torch.float16, device=dev)
+            for i in range(launches_of("gemv")):
+                q4.q4_gemv(x, copies[i % len(copies)], y=y)
+            sep()
+        del copies
     s = gemv_setup(q4, torch, dev, rotate_bytes)
-    for m in s["ms"]:
-        gemv_launches(q4, s, launches, [m], 0)()
-    torch.cuda.synchronize()
+    for m in ATTN_MS:
+        gemv_launches(q4, s, launches_of("gemv"), [m], 0)()
+        sep()
     ws = [torch.from_numpy(s["w_host"]).to(dev) for _ in range(2)]
-    for i in range(launches):
+    for i in range(launches_of("quantize")):
         q4.q4_quantize(ws[i % 2], packed=s["packed"][0])
+    sep()
     del s, ws
-    torch.cuda.synchronize()
+    m = 4096
+    x = torch.randn((m, lins["q"].k), device=dev, generator=gen).half()
+    xd = torch.randn((m, lins["down"].k), device=dev, generator=gen).half()
+    for g, _ in LAYER_GROUPS:
+        rows, k = group_shape(lins, g)
+        y = torch.empty((m, rows), dtype=torch.float16, device=dev)
+        for _ in range(launches_of("gemm")):
+            q4.q4_gemm(xd if g == "down" else x, bufs[g], y=y)
+        sep()
+    del x, xd, bufs
     _, _, _, whole, _ = gemm_setup(q4, torch, dev)
-    for _ in range(3):
+    for _ in range(launches_of("gemm")):
         whole()
+    sep()
     torch.cuda.synchronize()
     print("traffic launches done", flush=True)
 
 
+def mfma_keys():
+    return [f"gemm_layer_{g}_m4096" for g, _ in LAYER_GROUPS] + [
+        "gemm_2048x17408x5120", "gemm_8x256x17408x5120"]
+
+
 def mfma_run(q4, torch, dev, reps=3):
-    """The launches the matrix-core counter pass (MfmaUtil, MfmaFlopsF16) reads:
-    the 2048 x 17408 x 5120 prefill as one launch and as 8 chunks of 256 rows."""
+    """The launches the matrix-core counter pass (MfmaUtil, MfmaFlopsF16)
+    reads, in the order of mfma_keys(), a separator kernel after each group:
+    the layer's prefill launches at M = 4096, the 2048 x 17408 x 5120 prefill
+    as one launch and as 8 chunks of 256 rows (reps times each)."""
+    sep = separator(torch, dev)
+    lins, bufs, _ = layer_setup(q4, torch, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(8)
+    m = 4096
+    x = torch.randn((m, lins["q"].k), device=dev, generator=gen).half()
+    xd = torch.randn((m, lins["down"].k), device=dev, generator=gen).half()
+    for g, _ in LAYER_GROUPS:
+        rows, _k = group_shape(lins, g)
+        y = torch.empty((m, rows), dtype=torch.float16, device=dev)
+        for _ in range(reps):
+            q4.q4_gemm(xd if g == "down" else x, bufs[g], y=y)
+        sep()
+    del x, xd, bufs
     _, _, _, whole, chunked = gemm_setup(q4, torch, dev)
     for _ in range(reps):
         whole()
+    sep()
     for _ in range(reps):
         chunked(256)()
+    sep()
     torch.cuda.synchronize()
     print("mfma launches done", flush=True)
 
 
-def mfma_summary(csv_path, out_path):
-    """profiles/mfma.json from the counter pass over mfma_run: per GEMM kernel,
-    the median per dispatch of MfmaUtil (matrix-core busy cycles over the
-    dispatch's active cycles, all SIMDs) and of MfmaFlopsF16 (fp16 matrix
-    flops issued), with the algorithmic flops of the dispatch's share."""
+def _ours(name):
+    return "q4::" in name or name.startswith("_ZN2q4")
+
+
+def _kernel_label(name):
+    """A short label of one of this library's kernels from its (mangled or
+    demangled) name."""
     import re
-    by = {}
+    for pat, lab in (("gemm_mfma_kernel", "gemm_mfma"), ("gemm_slicek_kernel", "gemm_slicek"),
+                     ("gemm_exact_kernel", "gemm_exact"), ("gemm_tile_kernel", "gemm_tile"),
+                     ("splitk_reduce", "splitk_reduce"), ("bf16_rows_to_f16", "bf16_stage"),
+                     ("gemv_tile_kernel", "gemv_tile"), ("gemv_bal_kernel", "gemv_bal"),
+                     ("gemv_stream_kernel", "gemv_stream"), ("gemv_rowwave", "gemv_rowwave"),
+                     ("quantize", "quantize")):
+        if pat in name:
+            if lab == "gemm_mfma":
+                lab += "_256x256" if ("ILi256" in name or "<256" in name) else "_128x128"
+            if lab in ("gemm_mfma_256x256", "gemm_mfma_128x128", "gemm_slicek", "splitk_reduce"):
+                if re.search(r"kernelI(?:Li\d+E)*fE", name) or "float>" in name:
+                    lab += "_f32"
+            return lab
+    return "other"
+
+
+def _grouped(csv_path, counter, keys):
+    """Per launch group (keys, in order), per kernel label, the per-dispatch
+    values of one counter: the separator dispatches split the rows."""
+    out = {k: {} for k in keys}
+    i = 0
     for did, name, cnt, val in _pmc_rows(csv_path):
-        if "gemm_" not in name and "splitk_reduce" not in name:
+        if cnt != counter:
             continue
-        if "gemm_mfma_kernel" in name:
-            key = "gemm_mfma_256x256" if ("ILi256" in name or "<256" in name) else "gemm_mfma_128x128"
-        elif "gemm_slicek_kernel" in name:
-            key = "gemm_slicek_128x128"
-        elif "splitk_reduce" in name:
-            key = "splitk_reduce"
-        else:
-            key = "other_gemm"
-        # the output type is the kernels' last template argument: fp16 y, or
-        # fp32 split-K partials (the tail)
-        if re.search(r"kernelI(?:Li\d+E)*fE", name) or "float>" in name:
-            key += "_f32_partials"
-        else:
-            key += "_f16_out"
-        by.setdefault(key, {}).setdefault(cnt, []).append(val)
-    kernels = {}
-    for key, cnts in sorted(by.items()):
-        kernels[key] = {c: float(np.median(v)) for c, v in cnts.items()}
-        kernels[key]["dispatches"] = max(len(v) for v in cnts.values())
-    data = {"source_hash": kernel_source_hash(),
-            "workload": "prefill_2048x17408x5120, whole launch and 8 x 256-row chunks",
-            "peak_mfma_f16_tflops": MFMA_F16_PEAK_TFLOPS, "kernels": kernels}
-    Path(out_path).write_text(json.dumps(data, indent=1) + "\n")
-    return data
+        if SEPARATOR in name:
+            i += 1
+            continue
+        if i >= len(keys):
+            break
+        key = keys[i]
+        if key == "calib_copy":
+            if "neg" in name:
+                out[key].setdefault("neg", []).append(val)
+            continue
+        if _ours(name):
+            out[key].setdefault(_kernel_label(name), []).append(val)
+    return out
 
 
 def _pmc_rows(csv_path):
@@ -681,39 +967,30 @@ def _pmc_rows(csv_path):
     return rows
 
 
-def _traffic_key(name):
-    """Workload of a dispatch in the traffic_run launches (None: not counted)."""
-    if "neg_kernel" in name:
-        return "calib_copy"
-    if "gemv_" in name and "_kernel" in name:
-        return "gemv"
-    if "quantize_kernel" in name:
-        return "quantize_fp32_5120x5120"
-    if "gemm_mfma_kernelILi256" in name or "gemm_mfma_kernel<256" in name:
-        return "gemm_2048x17408x5120"
-    return None
-
-
-def _traffic_groups(csv_path, counter):
-    """Per workload, the per-dispatch values of one counter of a traffic_run
-    pass.  GEMV dispatches are attributed to batch sizes by launch order
-    (traffic_run launches them in WORKLOADS[2].ms order)."""
-    import synth
-    ms = list(synth.WORKLOADS[2].ms)
-    by, gemv = {}, []
-    for did, name, cnt, val in _pmc_rows(csv_path):
-        if cnt != counter:
-            continue
-        key = _traffic_key(name)
-        if key == "gemv":
-            gemv.append(val)
-        elif key:
-            by.setdefault(key, []).append(val)
-    if gemv:
-        per = len(gemv) // len(ms)
-        for i, m in enumerate(ms):
-            by[f"gemv_5120x5120_m{m}"] = gemv[i * per:(i + 1) * per]
-    return by
+def mfma_summary(csv_path, out_path):
+    """profiles/mfma.json from the counter pass over mfma_run: per launch group
+    and kernel, the median per dispatch of MfmaUtil (matrix-core busy cycles
+    over the dispatch's active cycles) and of MfmaFlopsF16 (fp16 matrix flops
+    issued)."""
+    keys = mfma_keys()
+    groups = {}
+    for cnt in ("MfmaUtil", "MfmaFlopsF16"):
+        for key, by in _grouped(csv_path, cnt, keys).items():
+            for lab, vals in by.items():
+                e = groups.setdefault(key, {}).setdefault(lab, {})
+                e[cnt] = float(np.median(vals))
+                e["dispatches"] = len(vals)
+    kernels = {}
+    for key, by in groups.items():
+        # the group's kernel issuing the most matrix flops stands for it (the main tiles)
+        main = max(by.items(), key=lambda kv: kv[1].get("MfmaFlopsF16", 0.0))
+        kernels[key] = {"main_kernel": main[0], "MfmaUtil": main[1].get("MfmaUtil"), "by_kernel": by}
+    data = {"source_hash": kernel_source_hash(),
+            "workload": "bench.py --mfma: the layer prefill at M = 4096 (4 launches), and "
+                        "2048 x 17408 x 5120 whole and as 8 x 256-row chunks",
+            "peak_mfma_f16_tflops": MFMA_F16_PEAK_TFLOPS, "kernels": kernels}
+    Path(out_path).write_text(json.dumps(data, indent=1) + "\n")
+    return data
 
 
 SQ_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
@@ -722,14 +999,16 @@ SQ_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_
 
 def sq_summary(csv_path, out_path):
     """profiles/sq.json from one counter pass of SQ_COUNTERS over traffic_run:
-    per workload, the median per dispatch of each counter, and the ratios read
-    from them (waiting cycles per wave cycle; LDS bank-conflict cycles per
-    cycle of LDS instruction activity)."""
+    per launch group, the median per dispatch of each counter over the
+    group's kernels, and the ratios read from them (waiting cycles per wave
+    cycle; LDS bank-conflict cycles per cycle of LDS instruction activity)."""
+    keys = traffic_keys()
     kernels = {}
     for c in SQ_COUNTERS:
-        for key, vals in _traffic_groups(csv_path, c).items():
-            if key == "calib_copy":
+        for key, by in _grouped(csv_path, c, keys).items():
+            if key == "calib_copy" or not by:
                 continue
+            vals = [v for vs in by.values() for v in vs]
             kernels.setdefault(key, {})[c] = float(np.median(vals))
             kernels[key]["dispatches"] = len(vals)
     for v in kernels.values():
@@ -744,96 +1023,155 @@ def sq_summary(csv_path, out_path):
 
 
 def traffic_summary(fetch_csv, write_csv, out_path):
-    """profiles/traffic.json from the two counter passes: per kernel, the median
-    FETCH_SIZE and WRITE_SIZE per dispatch (KiB), each scaled by known bytes /
-    counted bytes of the plain copy.  GEMV dispatches are attributed to batch
-    sizes by launch order (traffic_run launches them in WORKLOADS[2].ms order)."""
-    def medians(path, counter):
-        by = _traffic_groups(path, counter)
-        return {k: float(np.median(v)) for k, v in by.items()}, {k: len(v) for k, v in by.items()}
-
-    fetch, nf = medians(fetch_csv, "FETCH_SIZE")
-    write, nw = medians(write_csv, "WRITE_SIZE")
-    f_scale = TRAFFIC_CALIB_BYTES / (fetch["calib_copy"] * 1024.0)
-    w_scale = TRAFFIC_CALIB_BYTES / (write["calib_copy"] * 1024.0)
+    """profiles/traffic.json from the two counter passes: per launch group, the
+    FETCH_SIZE and WRITE_SIZE of one launch (all its dispatches, KiB, summed
+    over the group and divided by its launches), each scaled by known bytes /
+    counted bytes of the plain copy."""
+    keys = traffic_keys()
+    fetch = _grouped(fetch_csv, "FETCH_SIZE", keys)
+    write = _grouped(write_csv, "WRITE_SIZE", keys)
+    calf = float(np.median(fetch["calib_copy"]["neg"]))
+    calw = float(np.median(write["calib_copy"]["neg"]))
+    f_scale = TRAFFIC_CALIB_BYTES / (calf * 1024.0)
+    w_scale = TRAFFIC_CALIB_BYTES / (calw * 1024.0)
     kernels = {}
-    for key in sorted(set(fetch) & set(write)):
-        if key == "calib_copy":
+    for key in keys[1:]:
+        if not fetch[key] or not write[key]:
             continue
-        fb = fetch[key] * 1024.0 * f_scale
-        wb = write[key] * 1024.0 * w_scale
+        nl = launches_of(key)
+        fk = sum(sum(v) for v in fetch[key].values()) / nl
+        wk = sum(sum(v) for v in write[key].values()) / nl
+        fb, wb = fk * 1024.0 * f_scale, wk * 1024.0 * w_scale
         kernels[key] = {"fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb,
-                        "fetch_kib_raw": fetch[key], "write_kib_raw": write[key],
-                        "dispatches": min(nf[key], nw[key])}
+                        "fetch_kib_raw": fk, "write_kib_raw": wk,
+                        "dispatches_per_launch": {lab: len(v) / nl for lab, v in fetch[key].items()}}
     data = {"source_hash": kernel_source_hash(),
-            "calibration": {"bytes": TRAFFIC_CALIB_BYTES, "fetch_kib": fetch["calib_copy"],
-                            "write_kib": write["calib_copy"], "fetch_scale": f_scale,
-                            "write_scale": w_scale},
+            "calibration": {"bytes": TRAFFIC_CALIB_BYTES, "fetch_kib": calf, "write_kib": calw,
+                            "fetch_scale": f_scale, "write_scale": w_scale},
             "kernels": kernels}
     Path(out_path).write_text(json.dumps(data, indent=1) + "\n")
     return data
 
 
 def trace_summary(trace_csv, steps, warmup):
-    """Per batch size, the mean duration of the GEMV dispatches that bench_gemv
-    times, from a rocprofv3 kernel-trace CSV of a run with the same steps and
-    warmup.  bench_gemv is the run's first GEMV work: (2 max(warmup, 1) +
-    2 steps) len(ms) dispatches for the whole-step graphs (eager capture runs,
-    then the replays), then per batch size in WORKLOADS[2].ms order `steps`
-    eager launches (capture), `steps` in the warm replay and `steps` in the
-    timed replay.  Later legs (layer decode, bf16) launch more GEMVs after
-    these."""
+    """Per headline launch (group, batch size), the mean duration of the GEMV
+    dispatches that bench_headline_decode times, from a rocprofv3 kernel-trace
+    CSV of a default run with the same steps and warmup.  bench_headline_decode
+    is the run's first GEMV work: 2 (max(warmup, 1) + steps) steps of 8 launches
+    for the step graphs (eager capture runs, then the replays), then per group
+    and batch size `steps` eager launches (capture), `steps` in the warm replay
+    and `steps` in the timed replay, in LAYER_GROUPS x DECODE_MS order."""
     import csv
-    import synth
-    ms = list(synth.WORKLOADS[2].ms)
     rows = []
     with open(trace_csv) as f:
         for r in csv.DictReader(f):
             name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
-            # this library's kernels (demangled when launched directly, mangled
-            # when replayed from a graph)
-            ours = "q4::" in name or name.startswith("_ZN2q4")
-            if ours and "gemv_" in name and "_kernel" in name:
+            if _ours(name) and "gemv_" in name and "_kernel" in name:
                 start = int(r.get("Start_Timestamp") or r.get("Start-Timestamp"))
                 end = int(r.get("End_Timestamp") or r.get("End-Timestamp"))
                 rows.append((start, end - start, name))
     rows.sort()
-    first = (2 * max(warmup, 1) + 2 * steps) * len(ms)
-    tail = rows[first:first + 3 * steps * len(ms)]
-    out = []
-    for i, m in enumerate(ms):
-        rep = tail[(3 * i + 2) * steps:(3 * i + 3) * steps]
-        names = sorted({r[2] for r in rep})
-        out.append({"m": m, "dispatches": len(rep), "mean_us": float(np.mean([r[1] for r in rep])) / 1e3,
-                    "kernels": names})
+    per_step = len(LAYER_GROUPS) * len(DECODE_MS)
+    first = 2 * (max(warmup, 1) + steps) * per_step
+    out, i = [], first
+    for g, _ in LAYER_GROUPS:
+        for m in DECODE_MS:
+            rep = rows[i + 2 * steps:i + 3 * steps]
+            i += 3 * steps
+            out.append({"group": g, "m": m, "dispatches": len(rep),
+                        "mean_us": float(np.mean([r[1] for r in rep])) / 1e3 if rep else None,
+                        "kernels": sorted({r[2] for r in rep})})
     return out
 
 
-def cpu_baseline(w_host, n, k, ms, budget_s=12.0):
-    """The oracle, untuned, on the decode step (all four batch sizes)."""
+def cpu_baseline(budget_s=1.0):
+    """The oracle, as it stands, per configuration: quantise and matmul on
+    bounded samples of each configuration's own seeded inputs (a seeded
+    subset of weight rows; every configuration's batch sizes), with the BLAS
+    thread pool set to the cores this process may run on.  Each sample is
+    repeated for about budget_s seconds and scaled to the configuration's
+    units.  `value` is the layer decode step's packed-weight GB/s, the
+    headline's unit."""
     import oracle
     import synth
-    wl = synth.WORKLOADS[2]
-    packed = oracle.quantize(w_host)
-    xs = {m: synth.workload_activations(wl, k, m) for m in ms}
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    t0 = time.perf_counter()
-    steps = 0
-    while True:
-        for m in ms:
-            oracle.matmul_ref(xs[m], packed, n, k)
-        steps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = (time.perf_counter() - t0) / steps
-    wbytes = n * (k // QK) * BLOCK_BYTES
-    return {"value": wbytes * len(ms) / el / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{steps} full decode steps (M={ms}) of the 5120x5120 workload, "
-                      f"{el:.2f} s per step"}
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        limiter = None
+
+    def rep(fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                return el / n
+
+    def sample_rows(w, rows):
+        rng = np.random.default_rng(w.shape[0])
+        return np.ascontiguousarray(w[np.sort(rng.choice(w.shape[0], size=min(rows, w.shape[0]),
+                                                         replace=False))])
+
+    per = []
+    try:
+        for wid in (1, 2, 3, 4):
+            wl = synth.WORKLOADS[wid]
+            lin = wl.linears[0]
+            w = sample_rows(synth.workload_weights(wl, lin), 1024 if wid != 4 else 256)
+            r = w.shape[0]
+            tq = rep(lambda: oracle.quantize(w))
+            packed = oracle.quantize(w)
+            row = {"config": wl.name, "rows_sampled": r, "of_rows": lin.n,
+                   "quantize_mweights_per_s": r * lin.k / tq / 1e6}
+            mm = {}
+            for m in wl.ms:
+                x = synth.workload_activations(wl, lin.k, m)
+                t = rep(lambda: oracle.matmul_ref(x, packed, r, lin.k))
+                mm[f"m{m}"] = {"weight_gbs": packed_bytes(r, lin.k) / t / 1e9,
+                               "gflops": 2.0 * m * r * lin.k / t / 1e9,
+                               "full_config_s": t * lin.n / r}
+            row["matmul"] = mm
+            per.append(row)
+            del w, packed
+        wl = synth.WORKLOADS[5]
+        row = {"config": wl.name, "rows_sampled_per_linear": 512, "matmul": {}}
+        samples = {}
+        tq_tot, wq = 0.0, 0
+        for lin in wl.linears:
+            w = sample_rows(synth.workload_weights(wl, lin), 512)
+            tq_tot += rep(lambda: oracle.quantize(w)) if lin.name in ("q", "down") else 0.0
+            wq += w.size if lin.name in ("q", "down") else 0
+            samples[lin.name] = (oracle.quantize(w), lin)
+            del w
+        row["quantize_mweights_per_s"] = wq / tq_tot / 1e6
+        for m in (1, 10, 256):
+            xs = {kk: synth.workload_activations(wl, kk, m) for kk in {l.k for l in wl.linears}}
+
+            def layer():
+                for packed, lin in samples.values():
+                    oracle.matmul_ref(xs[lin.k], packed, packed.shape[0], lin.k)
+
+            t = rep(layer)
+            wb = sum(packed_bytes(p.shape[0], l.k) for p, l in samples.values())
+            fl = sum(2.0 * m * p.shape[0] * l.k for p, l in samples.values())
+            row["matmul"][f"m{m}"] = {"weight_gbs": wb / t / 1e9, "gflops": fl / t / 1e9}
+        per.append(row)
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+    dec = per[-1]["matmul"]
+    # the layer decode step (M = 1 and 10 back to back) at the oracle's rates
+    step_gbs = 2.0 / (1.0 / dec["m1"]["weight_gbs"] + 1.0 / dec["m10"]["weight_gbs"])
+    return {"value": step_gbs, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "per configuration, a seeded subset of weight rows (1024 rows of the "
+                      "single linears, 256 of the prefill weight, 512 of each layer linear) "
+                      "quantised and multiplied by the configuration's activations at each of "
+                      f"its batch sizes, each repeated for ~{budget_s:.0f} s; value: the layer "
+                      "decode step (M = 1 then 10) at the sampled rates",
+            "per_config": per}
 
 
 def main():
@@ -898,32 +1236,49 @@ def main():
         return
 
     out = {"metric": METRIC}
-    g = bench_gemv(q4, torch, dev, args.steps, args.warmup, rotate)
-    dom = max(g["per_m"], key=lambda r: r["mean_us"])  # the step's dominant launch
+    h = bench_headline_decode(q4, torch, dev, args.steps, args.warmup, rotate)
+    lins, bufs = h["lins"], h["bufs"]
+    dom = max(h["per_launch"], key=lambda r: r["mean_us"])  # the step's dominant launch
     out.update({
-        "value": g["value_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": g["step_s"] * 1e3, "higher_is_better": True,
+        "value": h["value_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": h["step_s"] * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": g["wl"].name, "n": g["n"], "k": g["k"], "ms": g["ms"],
+        "config": {"workload": "layer_27b_dense_7_linears: decode step, q/k/v and gate/up fused "
+                               "(4 q4_gemv launches per batch size)",
+                   "ms": h["ms"], "linears": {nm: [l.n, l.k] for nm, l in lins.items()},
+                   "groups": {g: list(group_shape(lins, g)) for g, _ in LAYER_GROUPS},
+                   "weights": "Student-t(3) x 0.02, quantised by q4_quantize",
                    "x_dtype": "f16", "y_dtype": "f16",
-                   "weight_copies_rotated": g["ncopies"],
-                   "weight_bytes_per_launch": g["wbytes"]},
+                   "weight_bytes_per_batch_size": h["layer_bytes"],
+                   "layer_copies_rotated": h["ncopies"]},
         "roofline": {"bound": "hbm", "achieved": dom["alg_gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": dom["alg_gbs"] / HBM_PEAK_GBS,
-                     "traffic": load_traffic(f"gemv_5120x5120_m{dom['m']}"),
-                     "kernel": f"q4_gemv m={dom['m']}", "mean_us": dom["mean_us"],
-                     "alg_bytes_per_launch": dom["alg_bytes"]},
-        "per_m": g["per_m"],
+                     "traffic": load_traffic(f"gemv_layer_{dom['group']}_m{dom['m']}"),
+                     "kernel": f"q4_gemv {dom['group']} m={dom['m']} ({dom['n']}x{dom['k']})",
+                     "mean_us": dom["mean_us"], "alg_bytes_per_launch": dom["alg_bytes"]},
+        "per_launch": h["per_launch"],
     })
-    out["gemv_dense_fp16_library"] = bench_gemv_dense_library(
-        torch, dev, g["setup"], g["per_m"], args.steps, rotate)
+    floor = bench_read_floor(torch, bufs, rotate, min(args.steps, 100))
+    floor_step = sum(floor[g]["mean_us"] for g, _ in LAYER_GROUPS) * len(h["ms"])
+    out["read_floor"] = {"op": "libq4floor plain streaming read of each group's packed buffer, "
+                               "rotated like the GEMV's copies, best of grids "
+                               + "/".join(map(str, FLOOR_GRIDS)), "per_group": floor,
+                         "step_us": floor_step,
+                         "gemv_step_over_floor": h["step_s"] * 1e6 / floor_step}
+    out["gemm"] = bench_headline_prefill(q4, torch, dev, lins, bufs, args.gemm_reps)
+    if args.only in ("all", "gemm"):
+        out["gemm"]["prefill_2048x17408x5120"] = bench_gemm(q4, torch, dev, args.gemm_reps)
+    if args.only in ("all", "layer"):
+        out["layer_decode"] = bench_layer_decode(q4, torch, dev, lins, bufs, min(args.steps, 50), rotate)
+        out["layer_prefill"] = bench_layer_prefill(q4, torch, dev, lins, bufs, 3)
+    del h, bufs
+    torch.cuda.empty_cache()
+    g = bench_gemv(q4, torch, dev, args.steps, args.warmup, rotate)
+    out["attn_proj"] = {"workload": g["wl"].name, "n": g["n"], "k": g["k"], "ms": g["ms"],
+                        "weight_copies_rotated": g["ncopies"], "step_us": g["step_s"] * 1e6,
+                        "weight_gbs": g["value_gbs"], "per_m": g["per_m"]}
     if args.only in ("all", "quantize"):
         out["quantize"] = bench_quantize(q4, torch, dev, g["w_host"], 20, rotate)
-    if args.only in ("all", "gemm"):
-        out["gemm"] = bench_gemm(q4, torch, dev, args.gemm_reps)
-    if args.only in ("all", "layer"):
-        out["layer_decode"] = bench_layer_decode(q4, torch, dev, min(args.steps, 50), rotate)
-        out["layer_prefill"] = bench_layer_prefill(q4, torch, dev, 3)
     if args.only in ("all", "other"):
         out["other_configs"] = bench_other_configs(q4, torch, dev, args.steps, rotate)
     if args.only in ("all", "bf16"):
@@ -931,7 +1286,7 @@ def main():
     if args.only in ("all", "host"):
         out["host_twin"] = bench_host_twin(q4, torch, g["packed0"], g["n"], g["k"], g["ms"])
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(g["w_host"], g["n"], g["k"], g["ms"])
+        out["cpu_baseline"] = cpu_baseline()
     out["kernel_source_hash"] = kernel_source_hash()
     print(json.dumps(out), flush=True)
 

@@ -22,6 +22,8 @@ BUILD_DIR = PKG / "_build"
 LIB_PATH = PKG / "libq4.so"
 HOST_SRC = PKG / "host" / "q4_host.cpp"
 HOST_LIB_PATH = PKG / "libq4host.so"
+FLOOR_SRC = PKG / "floor" / "q4_read_floor.hip"
+FLOOR_LIB_PATH = PKG / "libq4floor.so"
 ARCH = os.environ.get("Q4_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [
@@ -82,10 +84,21 @@ def build_host(verbose: bool = False) -> Path:
     return HOST_LIB_PATH
 
 
+def build_floor(verbose: bool = False) -> Path:
+    """Compile the benchmark's plain-read kernel (floor/q4_read_floor.hip) into
+    libq4floor.so; returns its path."""
+    tmp = FLOOR_LIB_PATH.with_suffix(".so.tmp")
+    _run([_hipcc(), *COMMON_FLAGS, "-shared", str(FLOOR_SRC), "-o", str(tmp)], verbose)
+    os.replace(tmp, FLOOR_LIB_PATH)
+    return FLOOR_LIB_PATH
+
+
 def build(verbose: bool = False) -> Path:
     """Compile every csrc/*.hip for gfx950 and link libq4.so (and build the
-    host-CPU twin libq4host.so); returns libq4.so's path."""
+    host-CPU twin libq4host.so and the benchmark's plain-read libq4floor.so);
+    returns libq4.so's path."""
     build_host(verbose)
+    build_floor(verbose)
     hipcc = _hipcc()
     BUILD_DIR.mkdir(exist_ok=True)
     srcs = sorted(CSRC.glob("*.hip"))

@@ -140,6 +140,22 @@ def test_gemm_noalloc_argument_checks(q4lib):
     assert f"#define Q4_NOALLOC_SCRATCH_BYTES ({limit >> 20}u << 20)" in header
 
 
+def test_read_floor_library_exports_and_checks():
+    """libq4floor (the benchmark's plain-read kernel) exports the function its
+    header declares and refuses bad arguments before any launch."""
+    from bit_block_quantized_q4_amd.build import FLOOR_LIB_PATH
+    import bench
+    text = re.sub(r"/\*.*?\*/", "", (ROOT / "include" / "q4_read_floor.h").read_text(), flags=re.S)
+    assert re.findall(r"\b(q4_[a-z0-9_]+)\s*\(", text) == ["q4_read_floor"]
+    assert FLOOR_LIB_PATH.exists()
+    L = bench.floor_lib()
+    assert L.q4_read_floor(None, 16, A, 1, None) == 1
+    assert L.q4_read_floor(A, 16, None, 1, None) == 1
+    assert L.q4_read_floor(A + 4, 16, A, 1, None) == 1
+    assert L.q4_read_floor(A, 24, A, 1, None) == 1
+    assert L.q4_read_floor(A, 16, A, 0, None) == 1
+
+
 def test_binding_fails_loudly_without_library(q4lib, monkeypatch, tmp_path):
     monkeypatch.setattr(q4lib, "LIB_PATH", tmp_path / "missing.so")
     monkeypatch.setattr(q4lib, "_LIB", None)

@@ -14,7 +14,6 @@ import pytest
 ROOT = Path(__file__).resolve().parent.parent
 sys.path.insert(0, str(ROOT))
 import bench  # noqa: E402
-import synth  # noqa: E402
 
 GEMV = "void q4::(anonymous namespace)::gemv_bal_kernel<8, 4, 1, false>(...)"
 TILE = "void q4::(anonymous namespace)::gemv_tile_kernel<2, 1, 32, true, 8, 4, false, 32>(...)"
@@ -34,30 +33,49 @@ def write_csv(path, rows):
                 w.writerow([did, did, name, c, v])
 
 
-def traffic_rows(counter, gemv_vals, calib, quant, gemm):
-    """A traffic pass as traffic_run launches it: the copy, then per batch size
-    (in WORKLOADS[2].ms order) its GEMV dispatches, then the quantiser and the
-    GEMM, with unrelated kernels in between."""
+SEP = "void at::native::vectorized_elementwise_kernel<4, at::native::bitwise_not_kernel_cuda(...)"
+REDUCE = "void q4::(anonymous namespace)::splitk_reduce_kernel<_Float16>(...)"
+
+
+def kernel_for(key):
+    """A kernel name of the family a launch group dispatches."""
+    if key.startswith("gemv"):
+        return TILE
+    if key.startswith("quantize"):
+        return QUANT
+    return GEMM
+
+
+def grouped_rows(keys, per_key, counter):
+    """A counter pass as bench.py's --traffic / --mfma runs launch it: per key
+    launches_of(key) launches (GEMM launches as two dispatches, the main
+    kernel and the split-K reduction), a separator after each group, with
+    unrelated kernels in between.  per_key(key, i) -> the value of dispatch i."""
     rows, did = [], 1
-    rows.append((did, OTHER, {counter: 9e9})); did += 1
-    rows.append((did, NEG, {counter: calib})); did += 1
-    for v in gemv_vals:
-        rows.append((did, GEMV if v < 3000 else TILE, {counter: v})); did += 1
-    rows.append((did, QUANT, {counter: quant})); did += 1
-    rows.append((did, GEMM, {counter: gemm})); did += 1
+    for key in keys:
+        rows.append((did, OTHER, {counter: 9e9})); did += 1
+        n = bench.launches_of(key)
+        for i in range(n):
+            if key == "calib_copy":
+                rows.append((did, NEG, {counter: per_key(key, i)})); did += 1
+                continue
+            rows.append((did, kernel_for(key), {counter: per_key(key, i)})); did += 1
+            if key.startswith("gemm"):
+                rows.append((did, REDUCE, {counter: 1.0})); did += 1
+        rows.append((did, SEP, {counter: 7e9})); did += 1
     return rows
 
 
 def test_traffic_summary_attributes_and_scales(tmp_path):
-    ms = list(synth.WORKLOADS[2].ms)
-    per = 3
-    # each batch size's dispatches share a value; medians must pick them out
-    gemv_f = [1000.0 * (i + 1) for i in range(len(ms)) for _ in range(per)]
-    gemv_w = [10.0 * (i + 1) for i in range(len(ms)) for _ in range(per)]
-    calib_kib = bench.TRAFFIC_CALIB_BYTES / 1024.0 * 1.25   # counter reads 25% high
+    keys = bench.traffic_keys()
+    calib_kib = bench.TRAFFIC_CALIB_BYTES / 1024.0
+    fval = {k: 1000.0 * (i + 1) for i, k in enumerate(keys)}
+    fval["calib_copy"] = calib_kib * 1.25   # the counter reads 25% high
+    wval = {k: 10.0 * (i + 1) for i, k in enumerate(keys)}
+    wval["calib_copy"] = calib_kib
     fcsv, wcsv = tmp_path / "f.csv", tmp_path / "w.csv"
-    write_csv(fcsv, traffic_rows("FETCH_SIZE", gemv_f, calib_kib, 500.0, 7000.0))
-    write_csv(wcsv, traffic_rows("WRITE_SIZE", gemv_w, bench.TRAFFIC_CALIB_BYTES / 1024.0, 50.0, 70.0))
+    write_csv(fcsv, grouped_rows(keys, lambda k, i: fval[k], "FETCH_SIZE"))
+    write_csv(wcsv, grouped_rows(keys, lambda k, i: wval[k], "WRITE_SIZE"))
     out = tmp_path / "traffic.json"
     d = bench.traffic_summary(fcsv, wcsv, out)
     assert json.loads(out.read_text()) == d
@@ -65,41 +83,76 @@ def test_traffic_summary_attributes_and_scales(tmp_path):
     assert d["calibration"]["fetch_scale"] == pytest.approx(0.8)
     assert d["calibration"]["write_scale"] == pytest.approx(1.0)
     k = d["kernels"]
-    assert set(k) == {f"gemv_5120x5120_m{m}" for m in ms} | {"quantize_fp32_5120x5120",
-                                                             "gemm_2048x17408x5120"}
-    for i, m in enumerate(ms):
-        e = k[f"gemv_5120x5120_m{m}"]
-        assert e["dispatches"] == per
-        assert e["fetch_bytes"] == pytest.approx(1000.0 * (i + 1) * 1024 * 0.8)
-        assert e["write_bytes"] == pytest.approx(10.0 * (i + 1) * 1024)
+    assert set(k) == set(keys[1:])
+    for key in keys[1:]:
+        extra = 1.0 if key.startswith("gemm") else 0.0   # the reduction's dispatch
+        e = k[key]
+        assert e["fetch_bytes"] == pytest.approx((fval[key] + extra) * 1024 * 0.8)
+        assert e["write_bytes"] == pytest.approx((wval[key] + extra) * 1024)
         assert e["traffic_bytes"] == pytest.approx(e["fetch_bytes"] + e["write_bytes"])
-    assert k["quantize_fp32_5120x5120"]["fetch_bytes"] == pytest.approx(500.0 * 1024 * 0.8)
+    assert k["gemm_layer_gateup_m4096"]["dispatches_per_launch"] == {"gemm_mfma_256x256": 1.0,
+                                                                     "splitk_reduce": 1.0}
 
 
 def test_sq_summary_ratios(tmp_path):
-    ms = list(synth.WORKLOADS[2].ms)
-    rows, did = [], 1
-    for i, m in enumerate(ms):
-        for _ in range(2):
-            rows.append((did, GEMV, {"SQ_WAVE_CYCLES": 1000.0, "SQ_WAIT_ANY": 600.0 + i,
-                                     "SQ_WAIT_INST_ANY": 100.0, "SQ_ACTIVE_INST_LDS": 50.0,
-                                     "SQ_LDS_BANK_CONFLICT": 25.0 * (i + 1)}))
-            did += 1
-    rows.append((did, QUANT, {"SQ_WAVE_CYCLES": 400.0, "SQ_WAIT_ANY": 100.0,
-                              "SQ_WAIT_INST_ANY": 50.0, "SQ_ACTIVE_INST_LDS": 0.0,
-                              "SQ_LDS_BANK_CONFLICT": 0.0}))
+    keys = bench.traffic_keys()
+    counters = {"SQ_WAVE_CYCLES": lambda k, i: 1000.0, "SQ_WAIT_ANY": lambda k, i: 600.0 + keys.index(k),
+                "SQ_WAIT_INST_ANY": lambda k, i: 100.0, "SQ_ACTIVE_INST_LDS": lambda k, i: 50.0,
+                "SQ_LDS_BANK_CONFLICT": lambda k, i: 25.0 * keys.index(k)}
+    rows = []
+    for c, f in counters.items():
+        rows += [(did + 100000 * list(counters).index(c), name, cnt)
+                 for did, name, cnt in grouped_rows(keys, f, c)]
     p = tmp_path / "sq.csv"
     write_csv(p, rows)
     d = bench.sq_summary(p, tmp_path / "sq.json")
     k = d["kernels"]
-    for i, m in enumerate(ms):
-        e = k[f"gemv_5120x5120_m{m}"]
-        assert e["dispatches"] == 2
-        assert e["wait_any_per_wave_cycle"] == pytest.approx((600.0 + i) / 1000.0)
-        assert e["wait_inst_per_wave_cycle"] == pytest.approx(0.1)
-        assert e["lds_conflict_per_lds_active"] == pytest.approx(0.5 * (i + 1))
-    assert k["quantize_fp32_5120x5120"]["lds_conflict_per_lds_active"] is None
-    assert k["quantize_fp32_5120x5120"]["wait_any_per_wave_cycle"] == pytest.approx(0.25)
+    e = k["gemv_layer_gateup_m10"]
+    i = keys.index("gemv_layer_gateup_m10")
+    assert e["dispatches"] == bench.launches_of("gemv_layer_gateup_m10")
+    assert e["wait_any_per_wave_cycle"] == pytest.approx((600.0 + i) / 1000.0)
+    assert e["wait_inst_per_wave_cycle"] == pytest.approx(0.1)
+    assert e["lds_conflict_per_lds_active"] == pytest.approx(0.5 * i)
+    assert "calib_copy" not in k
+
+
+def test_mfma_summary_takes_the_main_kernel(tmp_path):
+    keys = bench.mfma_keys()
+    rows = []
+    for j, c in enumerate(("MfmaUtil", "MfmaFlopsF16")):
+        f = (lambda k, i: 40.0 + keys.index(k)) if c == "MfmaUtil" else (lambda k, i: 1e12)
+        rows += [(did + 100000 * j, name, cnt) for did, name, cnt in grouped_rows(keys, f, c)]
+    p = tmp_path / "mfma.csv"
+    write_csv(p, rows)
+    d = bench.mfma_summary(p, tmp_path / "mfma.json")
+    for i, key in enumerate(keys):
+        e = d["kernels"][key]
+        assert e["main_kernel"] == "gemm_mfma_256x256"
+        assert e["MfmaUtil"] == pytest.approx(40.0 + i)
+
+
+def test_trace_summary_picks_the_timed_replays(tmp_path):
+    steps, warmup = 4, 2
+    per_step = len(bench.LAYER_GROUPS) * len(bench.DECODE_MS)
+    p = tmp_path / "trace.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        t = 0
+        for _ in range(2 * (warmup + steps) * per_step):   # the step graphs
+            w.writerow([TILE, t, t + 999_000]); t += 1_000_000
+        for j in range(per_step):                            # per launch: eager, warm, timed
+            for phase in range(3):
+                for _ in range(steps):
+                    dur = 5000 * (j + 1) if phase == 2 else 1
+                    w.writerow([TILE, t, t + dur]); t += 1_000_000
+                    w.writerow([OTHER, t, t + 7]); t += 1_000_000
+    out = bench.trace_summary(p, steps, warmup)
+    assert [(r["group"], r["m"]) for r in out] == [(g, m) for g, _ in bench.LAYER_GROUPS
+                                                  for m in bench.DECODE_MS]
+    for j, r in enumerate(out):
+        assert r["dispatches"] == steps
+        assert r["mean_us"] == pytest.approx(5.0 * (j + 1))
 
 
 def test_committed_summaries_gate_on_the_source_hash(tmp_path, monkeypatch):
