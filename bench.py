@@ -948,7 +948,14 @@ def _grouped(csv_path, counter, keys):
                 out[key].setdefault("neg", []).append(val)
             continue
         if _ours(name):
-            out[key].setdefault(_kernel_label(name), []).append(val)
+            lab = _kernel_label(name)
+            # only the kernel family the group launches (set-up work such as
+            # quantising the weights shares the segment)
+            fam = key.split("_")[0]
+            if (fam == "gemv" and lab.startswith("gemv")) or (fam == "quantize" and lab == "quantize") or \
+               (fam == "gemm" and (lab.startswith("gemm") or lab in ("splitk_reduce", "splitk_reduce_f32",
+                                                                      "bf16_stage"))):
+                out[key].setdefault(lab, []).append(val)
     return out
 
 
@@ -1235,6 +1242,12 @@ def main():
         mfma_run(q4, torch, dev)
         return
 
+    t_start = time.perf_counter()
+
+    def progress(leg):
+        print(f"[bench] {leg} done at {time.perf_counter() - t_start:.1f} s", file=sys.stderr,
+              flush=True)
+
     out = {"metric": METRIC}
     h = bench_headline_decode(q4, torch, dev, args.steps, args.warmup, rotate)
     lins, bufs = h["lins"], h["bufs"]
@@ -1258,6 +1271,7 @@ def main():
                      "mean_us": dom["mean_us"], "alg_bytes_per_launch": dom["alg_bytes"]},
         "per_launch": h["per_launch"],
     })
+    progress("headline decode")
     floor = bench_read_floor(torch, bufs, rotate, min(args.steps, 100))
     floor_step = sum(floor[g]["mean_us"] for g, _ in LAYER_GROUPS) * len(h["ms"])
     out["read_floor"] = {"op": "libq4floor plain streaming read of each group's packed buffer, "
@@ -1265,18 +1279,22 @@ def main():
                                + "/".join(map(str, FLOOR_GRIDS)), "per_group": floor,
                          "step_us": floor_step,
                          "gemv_step_over_floor": h["step_s"] * 1e6 / floor_step}
+    progress("read floor")
     out["gemm"] = bench_headline_prefill(q4, torch, dev, lins, bufs, args.gemm_reps)
+    progress("headline prefill")
     if args.only in ("all", "gemm"):
         out["gemm"]["prefill_2048x17408x5120"] = bench_gemm(q4, torch, dev, args.gemm_reps)
     if args.only in ("all", "layer"):
         out["layer_decode"] = bench_layer_decode(q4, torch, dev, lins, bufs, min(args.steps, 50), rotate)
         out["layer_prefill"] = bench_layer_prefill(q4, torch, dev, lins, bufs, 3)
+    progress("layer legs")
     del h, bufs
     torch.cuda.empty_cache()
     g = bench_gemv(q4, torch, dev, args.steps, args.warmup, rotate)
     out["attn_proj"] = {"workload": g["wl"].name, "n": g["n"], "k": g["k"], "ms": g["ms"],
                         "weight_copies_rotated": g["ncopies"], "step_us": g["step_s"] * 1e6,
                         "weight_gbs": g["value_gbs"], "per_m": g["per_m"]}
+    progress("attn proj")
     if args.only in ("all", "quantize"):
         out["quantize"] = bench_quantize(q4, torch, dev, g["w_host"], 20, rotate)
     if args.only in ("all", "other"):
@@ -1285,6 +1303,7 @@ def main():
         out["bf16"] = bench_bf16(q4, torch, dev, g["setup"], args.steps, args.gemm_reps)
     if args.only in ("all", "host"):
         out["host_twin"] = bench_host_twin(q4, torch, g["packed0"], g["n"], g["k"], g["ms"])
+    progress("gpu legs")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     out["kernel_source_hash"] = kernel_source_hash()
