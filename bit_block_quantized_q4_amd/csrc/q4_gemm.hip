@@ -1156,23 +1156,22 @@ namespace {
 // Converted bf16 activations occupy the workspace's first bytes.
 int64_t bf16_stage_bytes(int64_t m, int64_t k) { return (m * k * 2 + 255) / 256 * 256; }
 
-// bf16 activations -> fp16 rows (round to nearest even), one wave per row,
-// four rows per workgroup.  A row that holds any value fp16 cannot represent
-// exactly (beyond its range, or off its subnormal grid) is written entirely
-// as NaN instead: every tile and K split that reads it then ends with
-// non-finite accumulators and is recomputed on the exact route from the bf16
-// original.  Both buffers are 16-byte aligned and k % 32 == 0.
+// bf16 activations -> fp16 rows (round to nearest even), one workgroup of
+// 256 threads per row (a 256-row chunk still fills the chip).  A row that
+// holds any value fp16 cannot represent exactly (beyond its range, or off its
+// subnormal grid) is written entirely as NaN instead: every tile and K split
+// that reads it then ends with non-finite accumulators and is recomputed on
+// the exact route from the bf16 original.  Both buffers are 16-byte aligned
+// and k % 32 == 0.
 __global__ __launch_bounds__(256) void bf16_rows_to_f16_kernel(const uint16_t* __restrict__ x,
                                                                uint16_t* __restrict__ out,
                                                                int64_t m, int64_t k) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= m) return;  // whole wave
+  const int64_t row = blockIdx.x;  // < m: one workgroup per row
   const u32x4* src = reinterpret_cast<const u32x4*>(x + row * k);
   u32x4* dst = reinterpret_cast<u32x4*>(out + row * k);
   const int64_t np = k / 8;  // 16-byte pieces
   bool inexact = false;
-  for (int64_t p = lane; p < np; p += kWave) {
+  for (int64_t p = threadIdx.x; p < np; p += 256) {
     u32x4 v = src[p];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1182,9 +1181,10 @@ __global__ __launch_bounds__(256) void bf16_rows_to_f16_kernel(const uint16_t* _
     }
     dst[p] = v;
   }
-  if (__ballot(inexact) != 0) {
+  // (a separate kernel with no dynamic LDS: __syncthreads_or's own LDS is fine)
+  if (__syncthreads_or(inexact)) {
     const u32x4 qnan = {0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u};
-    for (int64_t p = lane; p < np; p += kWave) dst[p] = qnan;  // after this lane's own stores
+    for (int64_t p = threadIdx.x; p < np; p += 256) dst[p] = qnan;  // after this thread's own stores
   }
 }
 
@@ -1221,8 +1221,7 @@ hipError_t launch_gemm(const void* x, DType xt, const uint8_t* packed, void* y,
     int64_t mm = m, kk = k;
     void* argv[] = {&src, &dst, &mm, &kk};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bf16_rows_to_f16_kernel),
-                                         dim3(static_cast<unsigned>((m + 3) / 4)), dim3(256), argv,
-                                         0, s);
+                                         dim3(static_cast<unsigned>(m)), dim3(256), argv, 0, s);
     if (e != hipSuccess) return e;
     xp = reinterpret_cast<const half_t*>(ws);
     workspace = gemm_plan(m, n, k).ws_bytes > 0 ? ws + bf16_stage_bytes(m, k) : nullptr;

@@ -49,7 +49,7 @@ def test_no_scratch_or_spills(src):
 
 
 @pytest.mark.parametrize("src,pattern", [("q4_gemv.hip", "gemv_bal_kernel"),
-                                         ("q4_gemv_tile.hip", "gemv_tile_kernel")])
+                                         ("q4_gemv_tile.hip", "gemv_tile")])
 def test_dynamic_lds_kernels_have_no_static_lds(src, pattern):
     """The decode kernels launch with all 160 KB of a CU's LDS as dynamic
     shared memory, so any static LDS (for example the reduction buffer behind
@@ -64,7 +64,7 @@ def test_dynamic_lds_kernels_have_no_static_lds(src, pattern):
 @pytest.mark.parametrize("src,pattern", [("q4_gemm.hip", "gemm_mfma_kernel"),
                                          ("q4_gemv.hip", "gemv_bal_kernel"),
                                          ("q4_gemv.hip", "gemv_stream_kernel"),
-                                         ("q4_gemv_tile.hip", "gemv_tile_kernel")])
+                                         ("q4_gemv_tile.hip", "gemv_tile")])
 def test_no_register_used_before_its_load_lands(src, pattern):
     ks = kernels(asm(src), pattern)
     assert ks, pattern
