@@ -64,7 +64,7 @@ __device__ __forceinline__ void unroll(F&& f) {
 // the last tile's rows past WR read bytes of the slot's activation area
 // (in bounds; they feed only outputs that are never stored), which lets
 // three slots of 5 tiles x 2 activation tiles fit the LDS.
-template <int T, int AT, int PB, int NW, int NP, int WR = 16 * T>
+template <int T, int AT, int PB, int NW, int NP, int WR = 16 * T, int XR = 16 * AT>
 struct TileGeo {
   static constexpr int nw = NW;
   static constexpr int lanes = (NW + NP) * kWave;         // threads of the workgroup
@@ -79,8 +79,9 @@ struct TileGeo {
   static constexpr int niw = (wpos + clanes - 1) / clanes;  // copy rounds (max per wave)
   static constexpr int wbytes = (16 * wpos + 255) / 256 * 256;
   static constexpr int xp = PB * kQK * 2 / 16;            // 16-byte pieces per activation row
-  static constexpr int nix_max = (16 * AT * xp + clanes - 1) / clanes;
-  static constexpr int xbytes = 16 * AT * xp * 16;
+  static_assert(XR >= 1 && XR <= 16 * AT, "activation rows of a slot");
+  static constexpr int nix_max = (XR * xp + clanes - 1) / clanes;
+  static constexpr int xbytes = XR * xp * 16;
   static constexpr int slot = wbytes + xbytes;
   static constexpr int red = T * AT * NW * kWave * 16;
   static constexpr int lds = kTSlots * slot > red ? kTSlots * slot : red;
@@ -103,11 +104,11 @@ struct TileGeo {
 // the copying waves convert their own pieces in LDS before the phase barrier
 // instead measured slower: 12.3 against 8.9 us at 5120 x 5120, m = 16, as it
 // delays the barrier and the next phase's copies.)
-template <int T, int AT, int PB, bool FULL, int NW, int NP, bool XB, int WR>
+template <int T, int AT, int PB, bool FULL, int NW, int NP, bool XB, int WR, int XR>
 __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
     const half_t* __restrict__ x, const uint8_t* __restrict__ W, void* __restrict__ y, int m,
     int64_t n, int64_t k, int y_f16, int rows) {
-  using G = TileGeo<T, AT, PB, NW, NP, WR>;
+  using G = TileGeo<T, AT, PB, NW, NP, WR, XR>;
   static_assert(!FULL || WR == 16 * T, "a full workgroup copies 16 T rows");
   constexpr int CW = G::cwaves;
   extern __shared__ __attribute__((aligned(16))) uint8_t tsm[];
@@ -338,13 +339,14 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
   }
 }
 
-template <int T, int AT, int PB, bool FULL, bool XB, int WR = 16 * T, int NW = 8, int NP = 4>
+template <int T, int AT, int PB, bool FULL, bool XB, int WR = 16 * T, int XR = 16 * AT,
+          int NW = 8, int NP = 4>
 hipError_t launch_tile_f(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
                          int64_t n, int64_t k, int rows, hipStream_t s) {
-  using G = TileGeo<T, AT, PB, NW, NP, WR>;
+  using G = TileGeo<T, AT, PB, NW, NP, WR, XR>;
   static_assert(G::lds <= kTLdsMax, "LDS budget");
   const void* fn =
-      reinterpret_cast<const void*>(&gemv_tile_kernel<T, AT, PB, FULL, NW, NP, XB, WR>);
+      reinterpret_cast<const void*>(&gemv_tile_kernel<T, AT, PB, FULL, NW, NP, XB, WR, XR>);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     const hipError_t e =
@@ -352,7 +354,7 @@ hipError_t launch_tile_f(const void* x, const uint8_t* packed, void* y, bool y_f
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  if (rows < 1 || rows > WR) return hipErrorInvalidValue;
+  if (rows < 1 || rows > WR || m > XR) return hipErrorInvalidValue;
   const int64_t grid = (n + rows - 1) / rows;
   const half_t* xp = static_cast<const half_t*>(x);
   int yf = y_f16 ? 1 : 0;
@@ -376,6 +378,14 @@ struct TilePlan {
 // Five row tiles with two activation tiles (m > 16) fit the LDS ring only
 // with at most this many weight rows per slot.
 constexpr int kT5AT2Rows = 68;
+// Up to this many activation rows, a slot's activation area holds only them
+// (rows past m read row m - 1), which leaves room in three slots for nine
+// row tiles: 144 rows per workgroup, so 34816 rows run as one round of 256
+// workgroups instead of two rounds of 80-row workgroups (28.4 -> 25.5 us at
+// m = 10).  Up to 16 rows, seven tiles fit.  Fewer, larger workgroups
+// stream faster here: each one pays a start-up and a drain.
+constexpr int kT9MaxM = 10;
+constexpr int kT7MaxM = 16;
 
 // Rows per workgroup: whole 16-row tiles, enough for one workgroup per
 // compute unit (capped where the LDS ring would not fit; larger matrices take
@@ -388,9 +398,16 @@ TilePlan tile_plan(int m, int64_t n, int64_t k) {
   const int64_t cu = device_cu_count();
   TilePlan p;
   p.AT = m > 16 ? 2 : 1;
-  const int tmax = p.AT == 1 ? 5 : 4;
-  int64_t tfull = ((n + 15) / 16 + cu - 1) / cu;
+  int64_t tfull = ((n + 15) / 16 + cu - 1) / cu;  // tiles per workgroup for one round
   if (tfull < 1) tfull = 1;
+  // Six or seven tiles for one round run on the seven-tile kernel (m <= 16);
+  // more on the nine-tile kernel (m <= 10), in one round if they fit.  Past
+  // one round, m = 11..16 keeps five tiles: a second round that holds few
+  // seven-tile workgroups measured slower than two rounds of five.
+  int tmax = 5;
+  if (p.AT == 2) tmax = 4;
+  else if (tfull <= 7 && m <= kT7MaxM) tmax = 7;
+  else if (m <= kT9MaxM) tmax = 9;
   const bool wide = tfull > tmax;
   if (tfull > tmax) tfull = tmax;
   p.PB = p.AT == 1 && tfull <= 2 && k % 1024 == 0 ? 32 : 16;
@@ -409,6 +426,9 @@ TilePlan tile_plan(int m, int64_t n, int64_t k) {
   }
   p.rows = static_cast<int>(rows);
   p.T = static_cast<int>((rows + 15) / 16);
+  // six to nine tiles run on the seven- or nine-tile kernel (rows past p.rows
+  // are not copied)
+  if (p.T > 5) p.T = p.T <= 7 ? 7 : 9;
   return p;
 }
 
@@ -420,6 +440,24 @@ hipError_t launch_tile_tt(const TilePlan& p, const void* x, const uint8_t* packe
     case 2: return launch_tile_t<2, AT, PB, XB>(x, packed, y, y_f16, m, n, k, p.rows, s);
     case 3: return launch_tile_t<3, AT, PB, XB>(x, packed, y, y_f16, m, n, k, p.rows, s);
     case 4: return launch_tile_t<4, AT, PB, XB>(x, packed, y, y_f16, m, n, k, p.rows, s);
+    case 7:
+      if constexpr (AT == 1 && PB == 16) {
+        if (p.rows == 112)
+          return launch_tile_f<7, 1, 16, true, XB, 112, kT7MaxM>(x, packed, y, y_f16, m, n, k,
+                                                                 p.rows, s);
+        return launch_tile_f<7, 1, 16, false, XB, 112, kT7MaxM>(x, packed, y, y_f16, m, n, k,
+                                                                p.rows, s);
+      }
+      return hipErrorInvalidValue;
+    case 9:
+      if constexpr (AT == 1 && PB == 16) {
+        if (p.rows == 144)
+          return launch_tile_f<9, 1, 16, true, XB, 144, kT9MaxM>(x, packed, y, y_f16, m, n, k,
+                                                                 p.rows, s);
+        return launch_tile_f<9, 1, 16, false, XB, 144, kT9MaxM>(x, packed, y, y_f16, m, n, k,
+                                                                p.rows, s);
+      }
+      return hipErrorInvalidValue;
     default:
       if constexpr (AT == 1 && PB == 16)
         return launch_tile_t<5, AT, PB, XB>(x, packed, y, y_f16, m, n, k, p.rows, s);

@@ -301,6 +301,34 @@ def test_matrix_core_tile_wide_two_activation_tiles(q4lib, gpu, m, n, k):
     assert_matmul_close(g[:, cols], x, packed, n, k, cols=cols, what=f"wide m{m} n{n} k{k}")
 
 
+# Seven- and nine-tile workgroups (m <= 16 and m <= 10): all 16 T rows
+# copied (rows past n re-read row n - 1), or fewer (the rest of the slot is
+# never stored); one round of workgroups or several; fp16 and bf16 inputs.
+SEVEN_NINE_CASES = [(10, 34816, 1024, "f16"), (10, 34816, 5120, "f16"), (7, 28672, 4096, "f16"),
+                    (16, 24576, 4096, "f16"), (16, 28000, 1536, "f16"), (9, 40000, 1024, "f16"),
+                    (12, 40000, 1024, "f16"), (10, 34816, 1024, "bf16"), (16, 24576, 1536, "bf16")]
+
+
+@pytest.mark.parametrize("m,n,k,xdt", SEVEN_NINE_CASES)
+def test_matrix_core_tile_seven_and_nine_tiles(q4lib, gpu, m, n, k, xdt):
+    import torch
+    w = synth.random_weights(31 * m + n + k, n, k, "student_t")
+    packed = oracle.quantize(w)
+    if xdt == "bf16":
+        xb = synth.random_activations(37 * m + k, m, k, "bf16")
+        y = to_host(q4lib.q4_gemv(to_dev_bf16(xb, gpu), to_dev(packed, gpu), y_dtype=torch.float32,
+                                  n=n, k=k))
+        x = oracle.widen_bf16(xb)
+    else:
+        x = synth.random_activations(37 * m + k, m, k, "f16")
+        y = run_gemv(q4lib, x, packed, n, k, "f32", gpu)
+    rng = np.random.default_rng(n + m)
+    cols = np.unique(np.concatenate([rng.choice(n, size=1200, replace=False), np.arange(0, n, 112),
+                                     np.arange(111, n, 112), np.arange(135, n, 136),
+                                     np.arange(143, n, 144), [n - 1]]))
+    assert_matmul_close(y[:, cols], x, packed, n, k, cols=cols, what=f"{xdt} m{m} n{n} k{k}")
+
+
 @pytest.mark.parametrize("m,n,k", [(4, 5120, 17408), (4, 300, 16384), (3, 1000, 17408), (4, 37, 17920)])
 def test_balanced_long_k(q4lib, gpu, m, n, k):
     """m <= 4 with long K: the staged activations (up to 140 KB) leave room for
