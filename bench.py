@@ -11,7 +11,12 @@ last-level cache.  `value` is the step's packed-weight GB/s; `roofline` is the
 step's dominant launch (algorithmic bytes: packed weights + x + y) against
 8 TB/s.  The W warm-up steps and the K timed steps are recorded into HIP
 graphs and replayed, so the HIP events around a replay time GPU work, not
-Python's launch latency.
+Python's launch latency.  Before a timed replay the same graph is replayed,
+untimed, for a fixed wall time (0.5 s before the step, 0.1 s before every
+other timed replay; Q4_BENCH_SETTLE_S sets the first, the rest scale with it):
+the shader clock follows the load with a delay, and a launch timed right
+after different work runs at whatever clock that work left (the decode
+launches measured up to 15 % slower that way).
 
 The GEMM half (`gemm`): the same layer's prefill at M = 4096 (four launches),
 TFLOP/s against the fp16 matrix-core peak, with its own roofline object on the
@@ -63,6 +68,7 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "Q4_0 GEMV weight GB/s + GEMM TFLOPS, as % of MI355X HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+SETTLE_S = float(os.environ.get("Q4_BENCH_SETTLE_S", "0.5"))  # untimed clock settle before timing
 MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 matrix peak
 BLOCK_BYTES, QK = 18, 32
 CHUNK_ROWS = (128, 256, 512)     # prefill chunk-size sweep over the 2048-row batch
@@ -120,14 +126,33 @@ def capture(torch, fn):
     return g
 
 
-def replay_seconds(torch, g):
-    """GPU time of one replay, from HIP events on the replay stream."""
+def settle(torch, g, seconds):
+    """Replay g (untimed) until `seconds` of wall time have passed, so the GPU
+    clock reaches its steady state under this load before anything is timed."""
+    t0 = time.perf_counter()
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
+def replay_seconds(torch, g, settle_s=None, mark=None):
+    """GPU time of one replay, from HIP events on the replay stream, after
+    untimed replays that settle the clock (settle_s of wall time, by default
+    SETTLE_S / 5).  mark(), if given, launches a marker kernel just before and
+    just after the timed replay (outside the events) for trace attribution."""
+    settle(torch, g, SETTLE_S / 5 if settle_s is None else settle_s)
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    if mark:
+        mark()
     s.record()
     g.replay()
     e.record()
+    if mark:
+        mark()
     torch.cuda.synchronize()
     return s.elapsed_time(e) * 1e-3
 
@@ -380,8 +405,9 @@ def bench_headline_decode(q4, torch, dev, steps, warmup, rotate_bytes, ms=(1, 10
     gw = capture(torch, step_fn(max(warmup, 1), 0))
     gt = capture(torch, step_fn(steps, max(warmup, 1) * len(ms)))
     gw.replay()
-    step_s = replay_seconds(torch, gt) / steps
+    step_s = replay_seconds(torch, gt, settle_s=SETTLE_S) / steps
     del gw, gt, layers
+    sep = separator(torch, dev)
     per_launch = []
     for g, _ in LAYER_GROUPS:
         rows, k = group_shape(lins, g)
@@ -391,8 +417,7 @@ def bench_headline_decode(q4, torch, dev, steps, warmup, rotate_bytes, ms=(1, 10
                 for i in range(steps):
                     launch(m, g, copies[i % len(copies)])
             gr = capture(torch, fn)
-            gr.replay()
-            t = replay_seconds(torch, gr) / steps
+            t = replay_seconds(torch, gr, mark=sep) / steps
             del gr
             wb = packed_bytes(rows, k)
             alg = wb + 2 * m * k + 2 * m * rows
@@ -433,7 +458,7 @@ def bench_read_floor(torch, bufs, rotate_bytes, reps):
         nb = buf.numel()
         sink = torch.empty(max(FLOOR_GRIDS) * 256, dtype=torch.int32, device=buf.device)
         best = None
-        for wg in FLOOR_GRIDS:
+        for gi, wg in enumerate(FLOOR_GRIDS):
             def fn(wg=wg):
                 st = torch.cuda.current_stream().cuda_stream
                 for i in range(reps):
@@ -442,7 +467,8 @@ def bench_read_floor(torch, bufs, rotate_bytes, reps):
                         raise RuntimeError(f"q4_read_floor returned {rc}")
             gr = capture(torch, fn)
             gr.replay()
-            t = replay_seconds(torch, gr) / reps
+            # the clock is settled once per group (the grids are one load)
+            t = replay_seconds(torch, gr, settle_s=None if gi == 0 else 0.0) / reps
             del gr
             if best is None or t < best[0]:
                 best = (t, wg)
@@ -1060,31 +1086,30 @@ def traffic_summary(fetch_csv, write_csv, out_path):
     return data
 
 
-def trace_summary(trace_csv, steps, warmup):
+def trace_summary(trace_csv):
     """Per headline launch (group, batch size), the mean duration of the GEMV
     dispatches that bench_headline_decode times, from a rocprofv3 kernel-trace
-    CSV of a default run with the same steps and warmup.  bench_headline_decode
-    is the run's first GEMV work: 2 (max(warmup, 1) + steps) steps of 8 launches
-    for the step graphs (eager capture runs, then the replays), then per group
-    and batch size `steps` eager launches (capture), `steps` in the warm replay
-    and `steps` in the timed replay, in LAYER_GROUPS x DECODE_MS order."""
+    CSV of a default run: each timed replay sits between two marker
+    (SEPARATOR) kernels, the run's first markers, in LAYER_GROUPS x DECODE_MS
+    order."""
     import csv
     rows = []
     with open(trace_csv) as f:
         for r in csv.DictReader(f):
             name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
-            if _ours(name) and "gemv_" in name and "_kernel" in name:
+            ours = _ours(name) and "gemv_" in name and "_kernel" in name
+            if ours or SEPARATOR in name:
                 start = int(r.get("Start_Timestamp") or r.get("Start-Timestamp"))
                 end = int(r.get("End_Timestamp") or r.get("End-Timestamp"))
-                rows.append((start, end - start, name))
+                rows.append((start, end - start, name, ours))
     rows.sort()
-    per_step = len(LAYER_GROUPS) * len(DECODE_MS)
-    first = 2 * (max(warmup, 1) + steps) * per_step
-    out, i = [], first
+    marks = [i for i, r in enumerate(rows) if not r[3]]
+    out, j = [], 0
     for g, _ in LAYER_GROUPS:
         for m in DECODE_MS:
-            rep = rows[i + 2 * steps:i + 3 * steps]
-            i += 3 * steps
+            rep = [r for r in rows[marks[2 * j] + 1:marks[2 * j + 1]] if r[3]] \
+                if 2 * j + 1 < len(marks) else []
+            j += 1
             out.append({"group": g, "m": m, "dispatches": len(rep),
                         "mean_us": float(np.mean([r[1] for r in rep])) / 1e3 if rep else None,
                         "kernels": sorted({r[2] for r in rep})})
@@ -1207,7 +1232,7 @@ def main():
     args = ap.parse_args()
 
     if args.trace_summary:
-        for r in trace_summary(args.trace_summary, args.steps, args.warmup):
+        for r in trace_summary(args.trace_summary):
             print(json.dumps(r))
         return
     if args.traffic_summary:

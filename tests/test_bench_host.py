@@ -132,22 +132,29 @@ def test_mfma_summary_takes_the_main_kernel(tmp_path):
 
 
 def test_trace_summary_picks_the_timed_replays(tmp_path):
-    steps, warmup = 4, 2
+    """Each timed replay sits between two marker kernels; the settle replays
+    and capture launches around them (any number) are not counted."""
+    steps = 4
     per_step = len(bench.LAYER_GROUPS) * len(bench.DECODE_MS)
     p = tmp_path / "trace.csv"
+    sep = "void at::native::bitwise_not_kernel<signed char>(...)"
     with open(p, "w", newline="") as f:
         w = csv.writer(f)
         w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
         t = 0
-        for _ in range(2 * (warmup + steps) * per_step):   # the step graphs
+        for _ in range(37 * per_step):                       # the step graphs, settled
             w.writerow([TILE, t, t + 999_000]); t += 1_000_000
-        for j in range(per_step):                            # per launch: eager, warm, timed
-            for phase in range(3):
-                for _ in range(steps):
-                    dur = 5000 * (j + 1) if phase == 2 else 1
-                    w.writerow([TILE, t, t + dur]); t += 1_000_000
-                    w.writerow([OTHER, t, t + 7]); t += 1_000_000
-    out = bench.trace_summary(p, steps, warmup)
+        for j in range(per_step):                            # per launch
+            for _ in range(steps * (3 + j)):                 # capture and settle replays
+                w.writerow([TILE, t, t + 1]); t += 1_000_000
+            w.writerow([sep, t, t + 3]); t += 1_000_000
+            for _ in range(steps):                           # the timed replay
+                w.writerow([TILE, t, t + 5000 * (j + 1)]); t += 1_000_000
+                w.writerow([OTHER, t, t + 7]); t += 1_000_000
+            w.writerow([sep, t, t + 3]); t += 1_000_000
+        for _ in range(50):                                  # later legs
+            w.writerow([TILE, t, t + 2]); t += 1_000_000
+    out = bench.trace_summary(p)
     assert [(r["group"], r["m"]) for r in out] == [(g, m) for g, _ in bench.LAYER_GROUPS
                                                   for m in bench.DECODE_MS]
     for j, r in enumerate(out):
