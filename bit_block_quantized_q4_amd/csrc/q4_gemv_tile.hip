@@ -63,7 +63,10 @@ __device__ __forceinline__ void unroll(F&& f) {
 // waves copy too).  WR (<= 16 T) is the weight rows a slot holds: below 16 T
 // the last tile's rows past WR read bytes of the slot's activation area
 // (in bounds; they feed only outputs that are never stored), which lets
-// three slots of 5 tiles x 2 activation tiles fit the LDS.
+// three slots of 5 tiles x 2 activation tiles fit the LDS.  XR (<= 16 AT)
+// is the activation rows a slot holds: a launch needs m <= XR, and operand
+// rows past m read row m - 1, so a smaller area (nine tiles with m <= 10)
+// leaves the LDS to weight rows.
 template <int T, int AT, int PB, int NW, int NP, int WR = 16 * T, int XR = 16 * AT>
 struct TileGeo {
   static constexpr int nw = NW;
