@@ -74,13 +74,50 @@ BLOCK_BYTES, QK = 18, 32
 CHUNK_ROWS = (128, 256, 512)     # prefill chunk-size sweep over the 2048-row batch
 
 
+def _code_tokens(text: str) -> str:
+    """C/C++ source without its comments, whitespace runs collapsed (string and
+    character literals kept as written)."""
+    out, code, i, n = [], [], 0, len(text)
+
+    def flush_code():
+        if code:
+            words = "".join(code).split()
+            if words:
+                out.append(" ".join(words))
+            code.clear()
+
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            flush_code()
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            code.append(" ")
+        else:
+            code.append(c)
+            i += 1
+    flush_code()
+    return " ".join(out)
+
+
 def kernel_source_hash() -> str:
+    """Hash of the library's sources as code: comments and layout do not count,
+    so counters taken before a comment-only edit stay valid."""
     h = hashlib.sha256()
     for p in sorted((ROOT / "bit_block_quantized_q4_amd" / "csrc").glob("*")):
         if p.suffix not in (".hip", ".hpp", ".h"):
             continue  # sources only (not compiler by-products left beside them)
         h.update(p.name.encode())
-        h.update(p.read_bytes())
+        h.update(_code_tokens(p.read_text()).encode())
     return h.hexdigest()[:16]
 
 

@@ -162,6 +162,17 @@ def test_trace_summary_picks_the_timed_replays(tmp_path):
         assert r["mean_us"] == pytest.approx(5.0 * (j + 1))
 
 
+def test_source_hash_ignores_comments_and_layout():
+    """Comment-only or whitespace-only edits keep the hash (and so the
+    committed counters); a code edit, even inside a string, changes it."""
+    code = 'int f(int a) {\n  return a + 1;  // one\n}\n/* note */ const char* s = "a // b";\n'
+    same = '/* header */\nint f(int a)\n{ return a +   1; }\n const char* s = "a // b"; // tail\n'
+    assert bench._code_tokens(code) == bench._code_tokens(same)
+    assert bench._code_tokens(code) != bench._code_tokens(code.replace("a + 1", "a + 2"))
+    assert bench._code_tokens(code) != bench._code_tokens(code.replace('"a // b"', '"a //  b"'))
+    assert "note" not in bench._code_tokens(code) and "one" not in bench._code_tokens(code)
+
+
 def test_committed_summaries_gate_on_the_source_hash(tmp_path, monkeypatch):
     """A summary taken from other kernel sources is never reported."""
     prof = tmp_path / "profiles"
