@@ -74,51 +74,13 @@ BLOCK_BYTES, QK = 18, 32
 CHUNK_ROWS = (128, 256, 512)     # prefill chunk-size sweep over the 2048-row batch
 
 
-def _code_tokens(text: str) -> str:
-    """C/C++ source without its comments, whitespace runs collapsed (string and
-    character literals kept as written)."""
-    out, code, i, n = [], [], 0, len(text)
-
-    def flush_code():
-        if code:
-            words = "".join(code).split()
-            if words:
-                out.append(" ".join(words))
-            code.clear()
-
-    while i < n:
-        c = text[i]
-        if c in "\"'":
-            j = i + 1
-            while j < n and text[j] != c:
-                j += 2 if text[j] == "\\" else 1
-            flush_code()
-            out.append(text[i:j + 1])
-            i = j + 1
-        elif text.startswith("//", i):
-            j = text.find("\n", i)
-            i = n if j < 0 else j
-        elif text.startswith("/*", i):
-            j = text.find("*/", i + 2)
-            i = n if j < 0 else j + 2
-            code.append(" ")
-        else:
-            code.append(c)
-            i += 1
-    flush_code()
-    return " ".join(out)
-
-
-def kernel_source_hash() -> str:
-    """Hash of the library's sources as code: comments and layout do not count,
-    so counters taken before a comment-only edit stay valid."""
-    h = hashlib.sha256()
-    for p in sorted((ROOT / "bit_block_quantized_q4_amd" / "csrc").glob("*")):
-        if p.suffix not in (".hip", ".hpp", ".h"):
-            continue  # sources only (not compiler by-products left beside them)
-        h.update(p.name.encode())
-        h.update(_code_tokens(p.read_text()).encode())
-    return h.hexdigest()[:16]
+def kernel_hash() -> str:
+    """Hash of the built libq4.so: committed counter summaries describe that
+    exact binary, and are reported only while it is the one that runs."""
+    p = ROOT / "bit_block_quantized_q4_amd" / "libq4.so"
+    if not p.exists():
+        return "unbuilt"
+    return hashlib.sha256(p.read_bytes()).hexdigest()[:16]
 
 
 def load_traffic(kernel_key: str):
@@ -131,7 +93,7 @@ def load_traffic(kernel_key: str):
         data = json.loads(f.read_text())
     except ValueError:
         return None
-    if data.get("source_hash") != kernel_source_hash():
+    if data.get("kernel_hash") != kernel_hash():
         return None
     return data.get("kernels", {}).get(kernel_key)
 
@@ -146,7 +108,7 @@ def load_mfma_util(kernel_key: str):
         data = json.loads(f.read_text())
     except ValueError:
         return None
-    if data.get("source_hash") != kernel_source_hash():
+    if data.get("kernel_hash") != kernel_hash():
         return None
     k = data.get("kernels", {}).get(kernel_key)
     return None if k is None else k.get("MfmaUtil")
@@ -968,6 +930,90 @@ def mfma_run(q4, torch, dev, reps=3):
     print("mfma launches done", flush=True)
 
 
+PHASE_SLOTS = 64  # per computing wave: entry, 31 barriers, 31 phase ends, exit
+
+
+def trace_lib():
+    """libq4trace.so: libq4 with the tile GEMV's computing waves recording the
+    shader clock per phase (a measurement build; only --phase-trace loads it)."""
+    import ctypes
+    import bit_block_quantized_q4_amd as q4
+    from bit_block_quantized_q4_amd.build import TRACE_LIB_PATH
+    L = ctypes.CDLL(str(TRACE_LIB_PATH))
+    for name, (res, args) in q4._SIGS.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    L.q4_phase_trace_set.restype = ctypes.c_int
+    L.q4_phase_trace_set.argtypes = [ctypes.c_void_p]
+    return L
+
+
+def phase_summary(stamps, nw=8):
+    """Per-phase medians over workgroups (shader-clock cycles) from a
+    [workgroups, nw, PHASE_SLOTS] array of one launch's stamps (zeros where
+    nothing was recorded): the time from entry to phase 0's barrier, each
+    period between consecutive barriers, each phase's products (its slowest
+    computing wave's end after the barrier), and entry to exit."""
+    T = np.asarray(stamps, dtype=np.int64)
+    T = T[T[:, 0, 0] > 0]  # workgroups that ran
+    n = int(np.count_nonzero(T[0, 0, 1:32]))  # phases recorded (at most 31)
+    bar = T[:, 0, 1:1 + n]
+    done = T[:, :nw, 32:32 + n].max(axis=1)
+    return {"workgroups": int(T.shape[0]), "phases": n,
+            "entry_to_first_barrier": float(np.median(bar[:, 0] - T[:, 0, 0])),
+            "period": [float(v) for v in np.median(np.diff(bar, axis=1), axis=0)],
+            "products": [float(v) for v in np.median(done - bar, axis=0)],
+            "entry_to_exit": float(np.median(T[:, 0, 63] - T[:, 0, 0]))}
+
+
+def phase_trace_run(q4, torch, dev, rotate_bytes, steps=50):
+    """The headline's m = 10 launches (the tile GEMV) on libq4trace.so, clock
+    settled: per group, the phase clocks of the last launch of a replay,
+    summarised by phase_summary, with the replay's mean launch time and the
+    shader clock sampled during the replays."""
+    import bit_block_quantized_q4_amd.build as qb
+    L = trace_lib()
+    saved = q4._LIB
+    q4._LIB = L
+    out = {}
+    try:
+        lins, bufs, _ = layer_setup(q4, torch, dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(9)
+        m = 10
+        for g, _ in LAYER_GROUPS:
+            rows, k = group_shape(lins, g)
+            x = torch.randn((m, k), device=dev, generator=gen).half()
+            y = torch.empty((m, rows), dtype=torch.float16, device=dev)
+            copies = rotated(torch, bufs[g], rotate_bytes)
+            buf = torch.zeros(((rows + 15) // 16 + 1) * 8 * PHASE_SLOTS, dtype=torch.int64, device=dev)
+
+            def fn(copies=copies, x=x, y=y):
+                for i in range(steps):
+                    q4.q4_gemv(x, copies[i % len(copies)], y=y)
+            gr = capture(torch, fn)
+            if L.q4_phase_trace_set(buf.data_ptr()) != 0:
+                raise RuntimeError("q4_phase_trace_set failed")
+            with ClockSampler() as clk:
+                t = replay_seconds(torch, gr) / steps
+            L.q4_phase_trace_set(None)
+            del gr
+            st = buf.view(-1, 8, PHASE_SLOTS).cpu().numpy()
+            summ = phase_summary(st)
+            summ.update({"group": g, "m": m, "n": rows, "k": k, "mean_us": t * 1e6,
+                         "clock": clk.summary()})
+            out[f"gemv_layer_{g}_m{m}"] = summ
+            print(json.dumps({kk: summ[kk] for kk in ("group", "mean_us", "workgroups", "phases")}),
+                  flush=True)
+            del copies, buf
+    finally:
+        q4._LIB = saved
+    data = {"kernel_hash": kernel_hash(), "trace_lib": qb.TRACE_LIB_PATH.name, "launches": out}
+    (ROOT / "profiles" / "phase_trace.json").write_text(json.dumps(data, indent=1) + "\n")
+    return data
+
+
 def _ours(name):
     return "q4::" in name or name.startswith("_ZN2q4")
 
@@ -1055,7 +1101,7 @@ def mfma_summary(csv_path, out_path):
         # the group's kernel issuing the most matrix flops stands for it (the main tiles)
         main = max(by.items(), key=lambda kv: kv[1].get("MfmaFlopsF16", 0.0))
         kernels[key] = {"main_kernel": main[0], "MfmaUtil": main[1].get("MfmaUtil"), "by_kernel": by}
-    data = {"source_hash": kernel_source_hash(),
+    data = {"kernel_hash": kernel_hash(),
             "workload": "bench.py --mfma: the layer prefill at M = 4096 (4 launches), and "
                         "2048 x 17408 x 5120 whole and as 8 x 256-row chunks",
             "peak_mfma_f16_tflops": MFMA_F16_PEAK_TFLOPS, "kernels": kernels}
@@ -1087,7 +1133,7 @@ def sq_summary(csv_path, out_path):
         v["wait_any_per_wave_cycle"] = v.get("SQ_WAIT_ANY", 0.0) / wc if wc else None
         v["wait_inst_per_wave_cycle"] = v.get("SQ_WAIT_INST_ANY", 0.0) / wc if wc else None
         v["lds_conflict_per_lds_active"] = v.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds if lds else None
-    data = {"source_hash": kernel_source_hash(), "counters": list(SQ_COUNTERS), "kernels": kernels}
+    data = {"kernel_hash": kernel_hash(), "counters": list(SQ_COUNTERS), "kernels": kernels}
     Path(out_path).write_text(json.dumps(data, indent=1) + "\n")
     return data
 
@@ -1115,7 +1161,7 @@ def traffic_summary(fetch_csv, write_csv, out_path):
         kernels[key] = {"fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb,
                         "fetch_kib_raw": fk, "write_kib_raw": wk,
                         "dispatches_per_launch": {lab: len(v) / nl for lab, v in fetch[key].items()}}
-    data = {"source_hash": kernel_source_hash(),
+    data = {"kernel_hash": kernel_hash(),
             "calibration": {"bytes": TRAFFIC_CALIB_BYTES, "fetch_kib": calf, "write_kib": calw,
                             "fetch_scale": f_scale, "write_scale": w_scale},
             "kernels": kernels}
@@ -1258,6 +1304,9 @@ def main():
                     help="run the launches the FETCH_SIZE / WRITE_SIZE counter passes read")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from the two counter passes")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="per-phase clocks of the m = 10 decode launches on libq4trace.so "
+                         "(writes profiles/phase_trace.json)")
     ap.add_argument("--mfma", action="store_true",
                     help="run the launches the MfmaUtil / MfmaFlopsF16 counter pass reads")
     ap.add_argument("--mfma-summary", metavar="PMC_CSV",
@@ -1302,6 +1351,9 @@ def main():
         return
     if args.mfma:
         mfma_run(q4, torch, dev)
+        return
+    if args.phase_trace:
+        phase_trace_run(q4, torch, dev, rotate)
         return
 
     t_start = time.perf_counter()
@@ -1368,7 +1420,7 @@ def main():
     progress("gpu legs")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
-    out["kernel_source_hash"] = kernel_source_hash()
+    out["kernel_hash"] = kernel_hash()
     print(json.dumps(out), flush=True)
 
 

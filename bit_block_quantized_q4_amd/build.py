@@ -24,6 +24,7 @@ HOST_SRC = PKG / "host" / "q4_host.cpp"
 HOST_LIB_PATH = PKG / "libq4host.so"
 FLOOR_SRC = PKG / "floor" / "q4_read_floor.hip"
 FLOOR_LIB_PATH = PKG / "libq4floor.so"
+TRACE_LIB_PATH = PKG / "libq4trace.so"
 ARCH = os.environ.get("Q4_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [
@@ -93,6 +94,24 @@ def build_floor(verbose: bool = False) -> Path:
     return FLOOR_LIB_PATH
 
 
+def build_trace(verbose: bool = False) -> Path:
+    """Link libq4trace.so: libq4's objects with the tile GEMV compiled with
+    -DQ4_PHASE_TRACE (its computing waves record per-phase clocks into a
+    buffer set by q4_phase_trace_set).  A measurement build for
+    `bench.py --phase-trace`; nothing else loads it.  Needs build()'s objects."""
+    hipcc = _hipcc()
+    src = CSRC / "q4_gemv_tile.hip"
+    obj = BUILD_DIR / "q4_gemv_tile_trace.o"
+    _run([hipcc, *COMMON_FLAGS, *PER_FILE_FLAGS.get(src.name, []), "-DQ4_PHASE_TRACE",
+          "-c", str(src), "-o", str(obj)], verbose)
+    objs = [BUILD_DIR / (s.stem + ".o") for s in sorted(CSRC.glob("*.hip")) if s.name != src.name]
+    tmp = TRACE_LIB_PATH.with_suffix(".so.tmp")
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp),
+          *map(str, objs), str(obj)], verbose)
+    os.replace(tmp, TRACE_LIB_PATH)
+    return TRACE_LIB_PATH
+
+
 def build(verbose: bool = False) -> Path:
     """Compile every csrc/*.hip for gfx950 and link libq4.so (and build the
     host-CPU twin libq4host.so and the benchmark's plain-read libq4floor.so);
@@ -116,6 +135,7 @@ def build(verbose: bool = False) -> Path:
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp),
           *map(str, objs)], verbose)
     os.replace(tmp, LIB_PATH)
+    build_trace(verbose)
     return LIB_PATH
 
 

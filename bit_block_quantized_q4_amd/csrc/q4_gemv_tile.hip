@@ -38,6 +38,32 @@ namespace q4 {
 namespace {
 
 constexpr int kTLdsMax = 160 * 1024;
+
+#ifdef Q4_PHASE_TRACE
+// Measurement build only (libq4trace.so, never libq4.so): each computing wave
+// records the shader clock (s_memtime) at entry (slot 0), after phase p's
+// barrier (1 + p) and after phase p's products (32 + p), p < 31, and at the
+// end (63), into a buffer the caller sets with q4_phase_trace_set:
+// [workgroup][computing wave][64] uint64.
+__device__ uint64_t* g_phase_trace = nullptr;
+// The buffer's address is read once, at entry (a store through it could
+// otherwise alias the variable and force a reload at every mark).
+#define Q4_PHASE_TRACE_BEGIN \
+  uint64_t* const phase_trace_ = wave < NW ? g_phase_trace : nullptr;
+#define Q4_PHASE_MARK(ev)                                                             \
+  do {                                                                                \
+    if (phase_trace_ != nullptr) {                                                    \
+      const uint64_t t_ = __builtin_amdgcn_s_memtime();                               \
+      if (lane == 0)                                                                  \
+        phase_trace_[(static_cast<int64_t>(blockIdx.x) * NW + wave) * 64 + (ev)] = t_; \
+    }                                                                                 \
+  } while (0)
+#else
+#define Q4_PHASE_TRACE_BEGIN
+#define Q4_PHASE_MARK(ev) \
+  do {                    \
+  } while (0)
+#endif
 // Phases resident in LDS.  (Deeper rings of smaller phases, 16 blocks in up
 // to seven slots, measured slower than three slots of 32 blocks at
 // 5120 x 5120: the per-phase barrier and fixed costs outweigh the extra
@@ -124,6 +150,8 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
   const int64_t rb = (k / kQK) * kBlockBytes;  // bytes per weight row
   const int nph = static_cast<int>(k / G::phase_k);
   const uint32_t smem = lds_addr(tsm);
+  Q4_PHASE_TRACE_BEGIN
+  Q4_PHASE_MARK(0);
 
   // Weight copies.  Slot piece i = (q CW + cwave) 64 + lane holds piece
   // i % wstride_pc of the phase's segment of row i / wstride_pc (the padding
@@ -300,8 +328,10 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
     for (int p = 0; p < nph; ++p) {
       __builtin_amdgcn_s_barrier();
       compiler_fence();
+      if (p < 31) Q4_PHASE_MARK(1 + p);
       compute(p, -1);
       compiler_fence();
+      if (p < 31) Q4_PHASE_MARK(32 + p);
     }
   }
 
@@ -335,6 +365,7 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
       else static_cast<float*>(y)[off] = sum;
     }
   }
+  Q4_PHASE_MARK(63);
   if constexpr (XB) {
     if (workgroup_any_flag(inexact, reinterpret_cast<uint32_t*>(tsm)))
       gemv_exact_rows_bf16<NW + NP>(reinterpret_cast<const uint16_t*>(x), W, y, y_f16, m, n, k, row0,
@@ -494,3 +525,11 @@ hipError_t launch_gemv_tile(const void* x, bool x_bf16, const uint8_t* packed, v
 }
 
 }  // namespace q4
+
+#ifdef Q4_PHASE_TRACE
+// Sets (or, with nullptr, clears) the buffer the measurement build's tile
+// kernels record their phase clocks into; returns 0, or 1 on a HIP error.
+extern "C" int q4_phase_trace_set(void* buf) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(q4::g_phase_trace), &buf, sizeof(buf)) == hipSuccess ? 0 : 1;
+}
+#endif

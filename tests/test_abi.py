@@ -156,6 +156,15 @@ def test_read_floor_library_exports_and_checks():
     assert L.q4_read_floor(A, 16, A, 0, None) == 1
 
 
+def test_trace_build_is_separate(q4lib):
+    """libq4trace.so (the measurement build) exports the phase-trace setter;
+    libq4.so, the product, does not."""
+    from bit_block_quantized_q4_amd.build import TRACE_LIB_PATH
+    assert TRACE_LIB_PATH.exists()
+    assert hasattr(ctypes.CDLL(str(TRACE_LIB_PATH)), "q4_phase_trace_set")
+    assert not hasattr(ctypes.CDLL(str(q4lib.LIB_PATH)), "q4_phase_trace_set")
+
+
 def test_binding_fails_loudly_without_library(q4lib, monkeypatch, tmp_path):
     monkeypatch.setattr(q4lib, "LIB_PATH", tmp_path / "missing.so")
     monkeypatch.setattr(q4lib, "_LIB", None)

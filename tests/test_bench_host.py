@@ -9,6 +9,7 @@ import subprocess
 import sys
 from pathlib import Path
 
+import numpy as np
 import pytest
 
 ROOT = Path(__file__).resolve().parent.parent
@@ -79,7 +80,7 @@ def test_traffic_summary_attributes_and_scales(tmp_path):
     out = tmp_path / "traffic.json"
     d = bench.traffic_summary(fcsv, wcsv, out)
     assert json.loads(out.read_text()) == d
-    assert d["source_hash"] == bench.kernel_source_hash()
+    assert d["kernel_hash"] == bench.kernel_hash()
     assert d["calibration"]["fetch_scale"] == pytest.approx(0.8)
     assert d["calibration"]["write_scale"] == pytest.approx(1.0)
     k = d["kernels"]
@@ -162,30 +163,49 @@ def test_trace_summary_picks_the_timed_replays(tmp_path):
         assert r["mean_us"] == pytest.approx(5.0 * (j + 1))
 
 
-def test_source_hash_ignores_comments_and_layout():
-    """Comment-only or whitespace-only edits keep the hash (and so the
-    committed counters); a code edit, even inside a string, changes it."""
-    code = 'int f(int a) {\n  return a + 1;  // one\n}\n/* note */ const char* s = "a // b";\n'
-    same = '/* header */\nint f(int a)\n{ return a +   1; }\n const char* s = "a // b"; // tail\n'
-    assert bench._code_tokens(code) == bench._code_tokens(same)
-    assert bench._code_tokens(code) != bench._code_tokens(code.replace("a + 1", "a + 2"))
-    assert bench._code_tokens(code) != bench._code_tokens(code.replace('"a // b"', '"a //  b"'))
-    assert "note" not in bench._code_tokens(code) and "one" not in bench._code_tokens(code)
+def test_phase_summary_reads_one_launch_of_stamps():
+    """Two workgroups ran (the third slot row is zeros): five phases 4000
+    cycles apart, products ending 3000-3007 cycles after each barrier."""
+    T = np.zeros((3, 8, bench.PHASE_SLOTS), dtype=np.int64)
+    for g in range(2):
+        T[g, :, 0] = 1000
+        for p in range(5):
+            T[g, 0, 1 + p] = 2000 + 4000 * p
+            T[g, :, 32 + p] = 5000 + 4000 * p + np.arange(8)
+        T[g, 0, 63] = 30000
+    d = bench.phase_summary(T)
+    assert d["workgroups"] == 2 and d["phases"] == 5
+    assert d["entry_to_first_barrier"] == 1000
+    assert d["period"] == [4000.0] * 4
+    assert d["products"] == [3007.0] * 5
+    assert d["entry_to_exit"] == 29000
 
 
-def test_committed_summaries_gate_on_the_source_hash(tmp_path, monkeypatch):
+def test_kernel_hash_follows_the_built_library(tmp_path, monkeypatch):
+    """The hash that gates committed counters is the built libq4.so's."""
+    pkg = tmp_path / "bit_block_quantized_q4_amd"
+    pkg.mkdir()
+    monkeypatch.setattr(bench, "ROOT", tmp_path)
+    assert bench.kernel_hash() == "unbuilt"
+    (pkg / "libq4.so").write_bytes(b"\x7fELF one")
+    h1 = bench.kernel_hash()
+    (pkg / "libq4.so").write_bytes(b"\x7fELF two")
+    assert bench.kernel_hash() != h1 and len(h1) == 16
+
+
+def test_committed_summaries_gate_on_the_kernel_hash(tmp_path, monkeypatch):
     """A summary taken from other kernel sources is never reported."""
     prof = tmp_path / "profiles"
     prof.mkdir()
     (prof / "traffic.json").write_text(json.dumps(
-        {"source_hash": "0" * 16, "kernels": {"x": {"traffic_bytes": 1.0}}}))
+        {"kernel_hash": "0" * 16, "kernels": {"x": {"traffic_bytes": 1.0}}}))
     (prof / "mfma.json").write_text(json.dumps(
-        {"source_hash": "0" * 16, "kernels": {"y": {"MfmaUtil": 50.0}}}))
+        {"kernel_hash": "0" * 16, "kernels": {"y": {"MfmaUtil": 50.0}}}))
     monkeypatch.setattr(bench, "ROOT", tmp_path)
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "1" * 16)
+    monkeypatch.setattr(bench, "kernel_hash", lambda: "1" * 16)
     assert bench.load_traffic("x") is None
     assert bench.load_mfma_util("y") is None
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    monkeypatch.setattr(bench, "kernel_hash", lambda: "0" * 16)
     assert bench.load_traffic("x") == {"traffic_bytes": 1.0}
     assert bench.load_mfma_util("y") == 50.0
 
