@@ -954,24 +954,57 @@ def phase_summary(stamps, nw=8):
     [workgroups, nw, PHASE_SLOTS] array of one launch's stamps (zeros where
     nothing was recorded): the time from entry to phase 0's barrier, each
     period between consecutive barriers, each phase's products (its slowest
-    computing wave's end after the barrier), and entry to exit."""
+    computing wave's end after the barrier), entry to exit, and the shader
+    clock over the launch (shader cycles per tick of the 100 MHz clock read
+    at entry and exit, in MHz)."""
     T = np.asarray(stamps, dtype=np.int64)
     T = T[T[:, 0, 0] > 0]  # workgroups that ran
-    n = int(np.count_nonzero(T[0, 0, 1:32]))  # phases recorded (at most 31)
+    n = int(np.count_nonzero(T[0, 0, 1:31]))  # phases recorded (at most 30)
     bar = T[:, 0, 1:1 + n]
     done = T[:, :nw, 32:32 + n].max(axis=1)
-    return {"workgroups": int(T.shape[0]), "phases": n,
-            "entry_to_first_barrier": float(np.median(bar[:, 0] - T[:, 0, 0])),
-            "period": [float(v) for v in np.median(np.diff(bar, axis=1), axis=0)],
-            "products": [float(v) for v in np.median(done - bar, axis=0)],
-            "entry_to_exit": float(np.median(T[:, 0, 63] - T[:, 0, 0]))}
+    ticks = T[:, 0, 62] - T[:, 0, 31]
+    ok = ticks > 0
+    sclk = (T[ok, 0, 63] - T[ok, 0, 0]) / ticks[ok] * 100.0
+    out = {"workgroups": int(T.shape[0]), "phases": n,
+           "entry_to_first_barrier": float(np.median(bar[:, 0] - T[:, 0, 0])),
+           "period": [float(v) for v in np.median(np.diff(bar, axis=1), axis=0)],
+           "products": [float(v) for v in np.median(done - bar, axis=0)],
+           "entry_to_exit": float(np.median(T[:, 0, 63] - T[:, 0, 0])),
+           "sclk_mhz": float(np.median(sclk)) if sclk.size else None}
+    # The 100 MHz clock is common to the whole device (the shader clock's
+    # counter is not): the launch's span from the first workgroup's entry to
+    # the last one's exit, the spread of entries, and the median and slowest
+    # workgroup, in microseconds.
+    if ok.all() and T.shape[0] > 0:
+        e, x = T[:, 0, 31], T[:, 0, 62]
+        out.update({"launch_span_us": float(x.max() - e.min()) / 100.0,
+                    "entry_spread_us": float(e.max() - e.min()) / 100.0,
+                    "workgroup_us_median": float(np.median(x - e)) / 100.0,
+                    "workgroup_us_max": float((x - e).max()) / 100.0})
+    return out
 
 
-def phase_trace_run(q4, torch, dev, rotate_bytes, steps=50):
+def merge_phase_summaries(summs):
+    """Element-wise medians of several launches' phase_summary results."""
+    out = {}
+    for key, v in summs[0].items():
+        vals = [s[key] for s in summs if key in s]
+        if isinstance(v, list):
+            out[key] = [float(np.median(c)) for c in zip(*vals)]
+        elif key in ("workgroups", "phases"):
+            out[key] = v
+        elif any(x is None for x in vals) or len(vals) != len(summs):
+            out[key] = None
+        else:
+            out[key] = float(np.median(vals))
+    return out
+
+
+def phase_trace_run(q4, torch, dev, rotate_bytes, steps=50, replays=5):
     """The headline's m = 10 launches (the tile GEMV) on libq4trace.so, clock
-    settled: per group, the phase clocks of the last launch of a replay,
-    summarised by phase_summary, with the replay's mean launch time and the
-    shader clock sampled during the replays."""
+    settled: per group, the phase clocks of the last launch of each of
+    `replays` graph replays, summarised by phase_summary and merged by
+    element-wise medians, with the replays' mean launch time."""
     import bit_block_quantized_q4_amd.build as qb
     L = trace_lib()
     saved = q4._LIB
@@ -995,17 +1028,18 @@ def phase_trace_run(q4, torch, dev, rotate_bytes, steps=50):
             gr = capture(torch, fn)
             if L.q4_phase_trace_set(buf.data_ptr()) != 0:
                 raise RuntimeError("q4_phase_trace_set failed")
-            with ClockSampler() as clk:
-                t = replay_seconds(torch, gr) / steps
+            summs, times = [], []
+            for r in range(replays):
+                times.append(replay_seconds(torch, gr, settle_s=SETTLE_S if r == 0 else None) / steps)
+                summs.append(phase_summary(buf.view(-1, 8, PHASE_SLOTS).cpu().numpy()))
             L.q4_phase_trace_set(None)
             del gr
-            st = buf.view(-1, 8, PHASE_SLOTS).cpu().numpy()
-            summ = phase_summary(st)
-            summ.update({"group": g, "m": m, "n": rows, "k": k, "mean_us": t * 1e6,
-                         "clock": clk.summary()})
+            summ = merge_phase_summaries(summs)
+            summ.update({"group": g, "m": m, "n": rows, "k": k,
+                         "mean_us": float(np.median(times)) * 1e6, "replays": replays})
             out[f"gemv_layer_{g}_m{m}"] = summ
-            print(json.dumps({kk: summ[kk] for kk in ("group", "mean_us", "workgroups", "phases")}),
-                  flush=True)
+            print(json.dumps({kk: summ.get(kk) for kk in ("group", "mean_us", "workgroups", "phases",
+                                                          "sclk_mhz", "launch_span_us")}), flush=True)
             del copies, buf
     finally:
         q4._LIB = saved

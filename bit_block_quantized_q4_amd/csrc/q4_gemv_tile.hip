@@ -42,26 +42,33 @@ constexpr int kTLdsMax = 160 * 1024;
 #ifdef Q4_PHASE_TRACE
 // Measurement build only (libq4trace.so, never libq4.so): each computing wave
 // records the shader clock (s_memtime) at entry (slot 0), after phase p's
-// barrier (1 + p) and after phase p's products (32 + p), p < 31, and at the
-// end (63), into a buffer the caller sets with q4_phase_trace_set:
+// barrier (1 + p) and after phase p's products (32 + p), p < 30, and at the
+// end (63), and the constant 100 MHz clock (s_memrealtime) at entry (31) and
+// at the end (62), so that the shader clock's rate over the launch is known,
+// into a buffer the caller sets with q4_phase_trace_set:
 // [workgroup][computing wave][64] uint64.
 __device__ uint64_t* g_phase_trace = nullptr;
 // The buffer's address is read once, at entry (a store through it could
 // otherwise alias the variable and force a reload at every mark).
 #define Q4_PHASE_TRACE_BEGIN \
   uint64_t* const phase_trace_ = wave < NW ? g_phase_trace : nullptr;
-#define Q4_PHASE_MARK(ev)                                                             \
+#define Q4_PHASE_STAMP(ev, clock)                                                     \
   do {                                                                                \
     if (phase_trace_ != nullptr) {                                                    \
-      const uint64_t t_ = __builtin_amdgcn_s_memtime();                               \
+      const uint64_t t_ = clock();                                                    \
       if (lane == 0)                                                                  \
         phase_trace_[(static_cast<int64_t>(blockIdx.x) * NW + wave) * 64 + (ev)] = t_; \
     }                                                                                 \
   } while (0)
+#define Q4_PHASE_MARK(ev) Q4_PHASE_STAMP(ev, __builtin_amdgcn_s_memtime)
+#define Q4_PHASE_MARK_RT(ev) Q4_PHASE_STAMP(ev, __builtin_amdgcn_s_memrealtime)
 #else
 #define Q4_PHASE_TRACE_BEGIN
 #define Q4_PHASE_MARK(ev) \
   do {                    \
+  } while (0)
+#define Q4_PHASE_MARK_RT(ev) \
+  do {                       \
   } while (0)
 #endif
 // Row tiles from which the end-of-launch sum takes a lane's whole fragment
@@ -155,6 +162,7 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
   const uint32_t smem = lds_addr(tsm);
   Q4_PHASE_TRACE_BEGIN
   Q4_PHASE_MARK(0);
+  Q4_PHASE_MARK_RT(31);
 
   // Weight copies.  Slot piece i = (q CW + cwave) 64 + lane holds piece
   // i % wstride_pc of the phase's segment of row i / wstride_pc (the padding
@@ -346,10 +354,10 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
     for (int p = 0; p < nph; ++p) {
       __builtin_amdgcn_s_barrier();
       compiler_fence();
-      if (p < 31) Q4_PHASE_MARK(1 + p);
+      if (p < 30) Q4_PHASE_MARK(1 + p);
       compute(p, -1);
       compiler_fence();
-      if (p < 31) Q4_PHASE_MARK(32 + p);
+      if (p < 30) Q4_PHASE_MARK(32 + p);
     }
   }
 
@@ -418,6 +426,7 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
     }
   }
   Q4_PHASE_MARK(63);
+  Q4_PHASE_MARK_RT(62);
   if constexpr (XB) {
     if (workgroup_any_flag(inexact, reinterpret_cast<uint32_t*>(tsm)))
       gemv_exact_rows_bf16<NW + NP>(reinterpret_cast<const uint16_t*>(x), W, y, y_f16, m, n, k, row0,

@@ -165,13 +165,17 @@ def test_trace_summary_picks_the_timed_replays(tmp_path):
 
 def test_phase_summary_reads_one_launch_of_stamps():
     """Two workgroups ran (the third slot row is zeros): five phases 4000
-    cycles apart, products ending 3000-3007 cycles after each barrier."""
+    cycles apart, products ending 3000-3007 cycles after each barrier; the
+    29000 shader cycles from entry to exit span 1450 ticks of the 100 MHz
+    clock, i.e. a 2000 MHz shader clock."""
     T = np.zeros((3, 8, bench.PHASE_SLOTS), dtype=np.int64)
     for g in range(2):
         T[g, :, 0] = 1000
+        T[g, 0, 31] = 777
         for p in range(5):
             T[g, 0, 1 + p] = 2000 + 4000 * p
             T[g, :, 32 + p] = 5000 + 4000 * p + np.arange(8)
+        T[g, 0, 62] = 777 + 1450
         T[g, 0, 63] = 30000
     d = bench.phase_summary(T)
     assert d["workgroups"] == 2 and d["phases"] == 5
@@ -179,6 +183,20 @@ def test_phase_summary_reads_one_launch_of_stamps():
     assert d["period"] == [4000.0] * 4
     assert d["products"] == [3007.0] * 5
     assert d["entry_to_exit"] == 29000
+    assert d["sclk_mhz"] == 2000.0
+    assert d["launch_span_us"] == 14.5 and d["entry_spread_us"] == 0.0
+    assert d["workgroup_us_median"] == 14.5 and d["workgroup_us_max"] == 14.5
+
+
+def test_merge_phase_summaries_takes_elementwise_medians():
+    a = {"workgroups": 4, "phases": 2, "entry_to_first_barrier": 10.0, "period": [5.0],
+         "products": [1.0, 2.0], "entry_to_exit": 100.0, "sclk_mhz": 2000.0}
+    b = dict(a, entry_to_first_barrier=30.0, period=[7.0], products=[3.0, 6.0], sclk_mhz=None)
+    c = dict(a, entry_to_first_barrier=20.0, period=[6.0], products=[2.0, 4.0], entry_to_exit=90.0)
+    d = bench.merge_phase_summaries([a, b, c])
+    assert d["entry_to_first_barrier"] == 20.0 and d["period"] == [6.0]
+    assert d["products"] == [2.0, 4.0] and d["entry_to_exit"] == 100.0
+    assert d["sclk_mhz"] is None and d["phases"] == 2 and d["workgroups"] == 4
 
 
 def test_kernel_hash_follows_the_built_library(tmp_path, monkeypatch):

@@ -41,3 +41,5 @@ def test_trace_build_matches_the_product_and_records_phases(q4lib, gpu, m, n, k)
         assert np.all(np.diff(bars) > 0)                     # barriers in order
         assert np.all(t[:, 32:32 + p] >= bars)               # products after their barrier
         assert t[0, 63] >= t[:, 32 + p - 1].max()              # exit after every wave's last phase
+        assert t[0, 62] > t[0, 31] > 0                         # constant-clock stamps at entry and exit
+    assert 100.0 < d["sclk_mhz"] < 3000.0                      # a shader clock MI355X can run at
