@@ -9,11 +9,12 @@
 // (rows spread over every compute unit) the last row tile is partial: its
 // unfilled rows hold stale bytes, feed only their own outputs and are never
 // stored.  K is walked in phases of PB blocks (32 PB weights).  For every
-// phase four copying waves copy, global -> LDS, the phase's weight bytes of
-// the R rows and the phase's activation columns (16-byte copies); three
-// phases are resident in a ring, so the copies of phases p + 1 and p + 2 are
-// in flight while eight computing waves work on phase p.  Within a phase
-// wave w owns blocks w PB / 8 .. (w + 1) PB / 8 - 1 for all 16 T rows;
+// phase NP copying waves (four; two where two workgroups share a compute
+// unit) copy, global -> LDS, the phase's weight bytes of the R rows and the
+// phase's activation columns (16-byte copies); three phases are resident in
+// a ring, so the copies of phases p + 1 and p + 2 are in flight while NW
+// computing waves (eight, or four) work on phase p.  Within a phase wave w
+// owns blocks w PB / NW .. (w + 1) PB / NW - 1 for all 16 T rows;
 // each (row tile, block) pair is one v_mfma_f32_16x16x32_f16 with 16
 // activation rows on the A side and 16 weight rows on the B side.  The
 // block's 32 codes enter as exact fp16 integers q - 8 (the 1024 + q / 64 + q
@@ -468,6 +469,7 @@ hipError_t launch_tile_t(const void* x, const uint8_t* packed, void* y, bool y_f
 
 struct TilePlan {
   int T, AT, PB, rows;
+  bool pair = false;  // two workgroups per compute unit (see kPairMaxRows)
 };
 
 // Five row tiles with two activation tiles (m > 16) fit the LDS ring only
@@ -481,6 +483,16 @@ constexpr int kT5AT2Rows = 68;
 // stream faster here: each one pays a start-up and a drain.
 constexpr int kT9MaxM = 10;
 constexpr int kT7MaxM = 16;
+// Past one round of nine-tile workgroups (m <= 10, more than 144 rows per
+// compute unit) the rows are instead split over two workgroups per compute
+// unit, both resident at once: up to 112 rows each in 8-block phases (three
+// slots of at most 26 KB), four computing and two copying waves.  A second
+// round of large workgroups would leave most of the chip idle while it runs:
+// 40000 x 5120 at m = 10 measured 40.5 -> 28.9 us, 49152 x 5120 41.3 ->
+// 35.5 us, 40000 x 1024 15.7 -> 9.5 us; 57344 x 8192, where the large
+// workgroups take three full rounds, 62.9 -> 61.5 us.
+constexpr int kPairMaxRows = 112;
+constexpr int kPairPB = 8;
 
 // Rows per workgroup: whole 16-row tiles, enough for one workgroup per
 // compute unit (capped where the LDS ring would not fit; larger matrices take
@@ -496,13 +508,25 @@ TilePlan tile_plan(int m, int64_t n, int64_t k) {
   int64_t tfull = ((n + 15) / 16 + cu - 1) / cu;  // tiles per workgroup for one round
   if (tfull < 1) tfull = 1;
   // Six or seven tiles for one round run on the seven-tile kernel (m <= 16);
-  // more on the nine-tile kernel (m <= 10), in one round if they fit.  Past
+  // more on the nine-tile kernel (m <= 10), in one round if they fit, and
+  // past one round on two workgroups per compute unit (kPairMaxRows).  Past
   // one round, m = 11..16 keeps five tiles: a second round that holds few
   // seven-tile workgroups measured slower than two rounds of five.
   int tmax = 5;
   if (p.AT == 2) tmax = 4;
   else if (tfull <= 7 && m <= kT7MaxM) tmax = 7;
   else if (m <= kT9MaxM) tmax = 9;
+  if (tmax == 9 && tfull > 9 && k % (kPairPB * kQK) == 0) {
+    int64_t rows = (n + 2 * cu - 1) / (2 * cu);
+    rows = (rows + 3) / 4 * 4;
+    if (rows <= kPairMaxRows) {
+      p.PB = kPairPB;
+      p.rows = static_cast<int>(rows);
+      p.T = static_cast<int>((rows + 15) / 16);  // 5 .. 7
+      p.pair = true;
+      return p;
+    }
+  }
   const bool wide = tfull > tmax;
   if (tfull > tmax) tfull = tmax;
   p.PB = p.AT == 1 && tfull <= 2 && k % 1024 == 0 ? 32 : 16;
@@ -566,6 +590,22 @@ hipError_t launch_tile_tt(const TilePlan& p, const void* x, const uint8_t* packe
 template <bool XB>
 hipError_t launch_tile_x(const TilePlan& p, const void* x, const uint8_t* packed, void* y,
                          bool y_f16, int m, int64_t n, int64_t k, hipStream_t s) {
+  if (p.pair) {
+    // two resident workgroups per compute unit: 4 computing + 2 copying waves
+    switch (p.T) {
+      case 5:
+        return launch_tile_f<5, 1, kPairPB, false, XB, 80, kT9MaxM, 4, 2>(x, packed, y, y_f16, m, n,
+                                                                           k, p.rows, s);
+      case 6:
+        return launch_tile_f<6, 1, kPairPB, false, XB, 96, kT9MaxM, 4, 2>(x, packed, y, y_f16, m, n,
+                                                                           k, p.rows, s);
+      case 7:
+        return launch_tile_f<7, 1, kPairPB, false, XB, 112, kT9MaxM, 4, 2>(x, packed, y, y_f16, m,
+                                                                            n, k, p.rows, s);
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
   if (p.AT == 2) return launch_tile_tt<2, 16, XB>(p, x, packed, y, y_f16, m, n, k, s);
   if (p.PB == 32) {
     if (p.T == 1) return launch_tile_t<1, 1, 32, XB>(x, packed, y, y_f16, m, n, k, p.rows, s);

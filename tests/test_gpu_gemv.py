@@ -329,6 +329,55 @@ def test_matrix_core_tile_seven_and_nine_tiles(q4lib, gpu, m, n, k, xdt):
     assert_matmul_close(y[:, cols], x, packed, n, k, cols=cols, what=f"{xdt} m{m} n{n} k{k}")
 
 
+# Past one round of nine-tile workgroups (m <= 10, more than 144 rows per
+# compute unit): two workgroups per compute unit of 72-112 rows (five to seven
+# tiles, the last one partial where the rows are not a multiple of 16), the
+# last workgroup ragged; 8-block phases, so k = 512 has two.
+PAIR_CASES = [(5, 40000, 1024, "f16"), (10, 45000, 1536, "f16"), (8, 57000, 1024, "f16"),
+              (6, 37000, 512, "f16"), (10, 38000, 2048, "bf16"), (9, 40000, 1024, "f16")]
+
+
+@pytest.mark.parametrize("m,n,k,xdt", PAIR_CASES)
+def test_matrix_core_tile_two_workgroups_per_cu(q4lib, gpu, m, n, k, xdt):
+    import torch
+    w = synth.random_weights(53 * m + n + k, n, k, "student_t")
+    packed = oracle.quantize(w)
+    if xdt == "bf16":
+        xb = synth.random_activations(59 * m + k, m, k, "bf16")
+        y = to_host(q4lib.q4_gemv(to_dev_bf16(xb, gpu), to_dev(packed, gpu), y_dtype=torch.float32,
+                                  n=n, k=k))
+        x = oracle.widen_bf16(xb)
+    else:
+        x = synth.random_activations(59 * m + k, m, k, "f16")
+        y = run_gemv(q4lib, x, packed, n, k, "f32", gpu)
+    rows = -(-(-(-n // 512)) // 4) * 4  # ceil(n / 512) rounded up to a multiple of 4
+    rng = np.random.default_rng(n + 7 * m)
+    cols = np.unique(np.concatenate([rng.choice(n, size=1200, replace=False), np.arange(0, n, rows),
+                                     np.arange(rows - 1, n, rows), np.arange(15, n, 16),
+                                     np.arange(n - 130, n)]))
+    assert_matmul_close(y[:, cols], x, packed, n, k, cols=cols, what=f"{xdt} m{m} n{n} k{k}")
+
+
+def test_bf16_beyond_fp16_on_two_workgroups_per_cu(q4lib, gpu):
+    """The two-workgroups-per-CU form with bf16 activations fp16 cannot hold:
+    every workgroup recomputes its rows on the exact route.  Sampled
+    outputs, every workgroup's first and last row among them."""
+    import torch
+    from test_gpu_gemm import bf16_beyond_fp16
+    m, n, k = 7, 38100, 1024
+    w = synth.random_weights(197, n, k, "student_t")
+    packed = oracle.quantize(w)
+    xb, _ = bf16_beyond_fp16(199, m, k)
+    y = to_host(q4lib.q4_gemv(to_dev_bf16(xb, gpu), to_dev(packed, gpu), y_dtype=torch.float32,
+                              n=n, k=k))
+    assert np.isfinite(y).all()
+    rows = 76
+    cols = np.unique(np.concatenate([np.arange(0, n, rows), np.arange(rows - 1, n, rows), [n - 1],
+                                     np.random.default_rng(3).choice(n, size=800, replace=False)]))
+    assert_matmul_close(y[:, cols], oracle.widen_bf16(xb), packed, n, k, cols=cols,
+                        what=f"bf16 range m{m} n{n} k{k}")
+
+
 @pytest.mark.parametrize("m,n,k", [(4, 5120, 17408), (4, 300, 16384), (3, 1000, 17408), (4, 37, 17920)])
 def test_balanced_long_k(q4lib, gpu, m, n, k):
     """m <= 4 with long K: the staged activations (up to 140 KB) leave room for
