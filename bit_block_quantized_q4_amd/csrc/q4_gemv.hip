@@ -711,13 +711,9 @@ template <int NW, int P, int MR, bool XB>
 hipError_t launch_bal_t(const void* x, const uint8_t* packed, void* y, bool y_f16, int m,
                         int64_t n, int64_t k, const BalPlan& p, hipStream_t s) {
   const void* fn = reinterpret_cast<const void*>(&gemv_bal_kernel<NW, P, MR, XB>);
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(kLdsMax));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_allowed{0};
+  const hipError_t e = allow_dynamic_lds(fn, static_cast<int>(kLdsMax), lds_allowed);
+  if (e != hipSuccess) return e;
   const half_t* xp = static_cast<const half_t*>(x);
   int rows = p.rows_per_wg, yf = y_f16 ? 1 : 0;
   void* argv[] = {&xp, const_cast<const uint8_t**>(&packed), &y, &m, &n, &k, &rows, &yf};

@@ -443,13 +443,9 @@ hipError_t launch_tile_f(const void* x, const uint8_t* packed, void* y, bool y_f
   static_assert(G::lds <= kTLdsMax, "LDS budget");
   const void* fn =
       reinterpret_cast<const void*>(&gemv_tile_kernel<T, AT, PB, FULL, NW, NP, XB, WR, XR>);
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    const hipError_t e =
-        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kTLdsMax);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_allowed{0};
+  const hipError_t e = allow_dynamic_lds(fn, kTLdsMax, lds_allowed);
+  if (e != hipSuccess) return e;
   if (rows < 1 || rows > WR || m > XR) return hipErrorInvalidValue;
   const int64_t grid = (n + rows - 1) / rows;
   const half_t* xp = static_cast<const half_t*>(x);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace q4 {
 
 constexpr int kQK = 32;          // weights per block
@@ -52,6 +54,20 @@ __device__ __forceinline__ bool f16x2_holds_bf16x2(uint32_t h, uint32_t v) {
   const half2_t hh = __builtin_bit_cast(half2_t, h);
   return static_cast<float>(hh[0]) == __builtin_bit_cast(float, v << 16) &&
          static_cast<float>(hh[1]) == __builtin_bit_cast(float, v & 0xFFFF0000u);
+}
+
+// Allows kernel `fn` up to `bytes` of dynamic LDS on the current device, once
+// per device (bit d of `done` records device d; devices past 63 set it on
+// every launch).  Safe to call from several host threads at once.
+inline hipError_t allow_dynamic_lds(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess) return ge;
+  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
 }
 
 // Launchers (return the launch status; never synchronise).
