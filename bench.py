@@ -20,10 +20,13 @@ launches measured up to 15 % slower that way).
 
 The GEMM half (`gemm`): the same layer's prefill at M = 4096 (four launches),
 TFLOP/s against the fp16 matrix-core peak, with its own roofline object on the
-dominant launch and the shader clock sampled during the leg.
+dominant launch and the shader clock sampled during the leg; `mfma_ceiling`
+times libq4floor's matrix-core kernel (the GEMM tile's fragment reads and
+products, nothing else) under the same kind of load, and the roofline object
+gives the dominant launch's fraction of that sustained rate too.
 
 The same JSON line carries:
-  read_floor     -- a plain library read (torch's sum) of the same rotated
+  read_floor     -- libq4floor's plain streaming read of the same rotated
                     packed buffers, launch by launch: what streaming these bytes
                     costs without any Q4_0 work;
   layer_decode   -- the layer as seven launches against four, M = 1 and 10;
@@ -432,14 +435,58 @@ def bench_headline_decode(q4, torch, dev, steps, warmup, rotate_bytes, ms=(1, 10
 
 
 def floor_lib():
-    """libq4floor.so (the plain-read kernel, include/q4_read_floor.h)."""
+    """libq4floor.so (the measurement kernels: the plain read of
+    include/q4_read_floor.h and the matrix-core ceiling of
+    include/q4_mfma_ceiling.h)."""
     import ctypes
     import torch  # noqa: F401  (its HIP runtime first, as for libq4)
     L = ctypes.CDLL(str(ROOT / "bit_block_quantized_q4_amd" / "libq4floor.so"))
     L.q4_read_floor.restype = ctypes.c_int
     L.q4_read_floor.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                 ctypes.c_void_p]
+    L.q4_mfma_ceiling.restype = ctypes.c_int
+    L.q4_mfma_ceiling.argtypes = [ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
     return L
+
+
+CEILING_WAVES, CEILING_PRODUCTS = 8, 8     # waves per workgroup, products per wave and step
+CEILING_FLOP = 2.0 * 32 * 32 * 16          # one v_mfma_f32_32x32x16_f16
+
+
+def ceiling_flop(workgroups, iters):
+    """Flops of one q4_mfma_ceiling launch."""
+    return float(workgroups) * CEILING_WAVES * iters * CEILING_PRODUCTS * CEILING_FLOP
+
+
+def bench_mfma_ceiling(torch, dev, reps=4, iters=4096, seed=0x5EED):
+    """The matrix cores' sustained rate under a long dense load: libq4floor's
+    ceiling kernel (the GEMM tile's fragment reads and fp16 matrix products,
+    nothing else) on one workgroup per compute unit, launches about as long
+    as the layer's gate/up GEMM, replayed back to back after the clock
+    settles; the shader clock is sampled meanwhile."""
+    L = floor_lib()
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(cu * 64 * CEILING_WAVES, dtype=torch.float32, device=dev)
+
+    def launch():
+        rc = L.q4_mfma_ceiling(seed, iters, sink.data_ptr(), cu, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"q4_mfma_ceiling returned {rc}")
+    t = time_gemm_calls(torch, launch, reps)
+    g = capture(torch, launch)
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 1.0:
+            for _ in range(20):
+                g.replay()
+            torch.cuda.synchronize()
+    del g, sink
+    tf = ceiling_flop(cu, iters) / t / 1e12
+    return {"op": "libq4floor q4_mfma_ceiling: v_mfma_f32_32x32x16_f16 with fragment reads "
+                  "from LDS, 8 waves per workgroup, one workgroup per compute unit",
+            "workgroups": cu, "iters": iters, "mean_us": t * 1e6, "tflops": tf,
+            "frac_mfma": tf / MFMA_F16_PEAK_TFLOPS, "clock": clk.summary()}
 
 
 FLOOR_GRIDS = (256, 512, 1024, 2048, 4096)
@@ -1429,6 +1476,10 @@ def main():
                          "gemv_step_over_floor": h["step_s"] * 1e6 / floor_step}
     progress("read floor")
     out["gemm"] = bench_headline_prefill(q4, torch, dev, lins, bufs, args.gemm_reps)
+    ceil = bench_mfma_ceiling(torch, dev)
+    out["gemm"]["mfma_ceiling"] = ceil
+    out["gemm"]["roofline"]["ceiling_tflops"] = ceil["tflops"]
+    out["gemm"]["roofline"]["frac_of_ceiling"] = out["gemm"]["roofline"]["achieved"] / ceil["tflops"]
     progress("headline prefill")
     if args.only in ("all", "gemm"):
         out["gemm"]["prefill_2048x17408x5120"] = bench_gemm(q4, torch, dev, args.gemm_reps)

@@ -22,7 +22,7 @@ BUILD_DIR = PKG / "_build"
 LIB_PATH = PKG / "libq4.so"
 HOST_SRC = PKG / "host" / "q4_host.cpp"
 HOST_LIB_PATH = PKG / "libq4host.so"
-FLOOR_SRC = PKG / "floor" / "q4_read_floor.hip"
+FLOOR_SRCS = (PKG / "floor" / "q4_read_floor.hip", PKG / "floor" / "q4_mfma_ceiling.hip")
 FLOOR_LIB_PATH = PKG / "libq4floor.so"
 TRACE_LIB_PATH = PKG / "libq4trace.so"
 ARCH = os.environ.get("Q4_OFFLOAD_ARCH", "gfx950")
@@ -86,10 +86,10 @@ def build_host(verbose: bool = False) -> Path:
 
 
 def build_floor(verbose: bool = False) -> Path:
-    """Compile the benchmark's plain-read kernel (floor/q4_read_floor.hip) into
-    libq4floor.so; returns its path."""
+    """Compile the benchmark's measurement kernels (floor/: the plain read and
+    the matrix-core ceiling) into libq4floor.so; returns its path."""
     tmp = FLOOR_LIB_PATH.with_suffix(".so.tmp")
-    _run([_hipcc(), *COMMON_FLAGS, "-shared", str(FLOOR_SRC), "-o", str(tmp)], verbose)
+    _run([_hipcc(), *COMMON_FLAGS, "-shared", *map(str, FLOOR_SRCS), "-o", str(tmp)], verbose)
     os.replace(tmp, FLOOR_LIB_PATH)
     return FLOOR_LIB_PATH
 
@@ -114,7 +114,7 @@ def build_trace(verbose: bool = False) -> Path:
 
 def build(verbose: bool = False) -> Path:
     """Compile every csrc/*.hip for gfx950 and link libq4.so (and build the
-    host-CPU twin libq4host.so and the benchmark's plain-read libq4floor.so);
+    host-CPU twin libq4host.so and the benchmark's measurement libq4floor.so);
     returns libq4.so's path."""
     build_host(verbose)
     build_floor(verbose)

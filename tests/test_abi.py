@@ -156,6 +156,19 @@ def test_read_floor_library_exports_and_checks():
     assert L.q4_read_floor(A, 16, A, 0, None) == 1
 
 
+def test_mfma_ceiling_exports_and_checks():
+    """libq4floor also exports the matrix-core ceiling its second header
+    declares, and refuses bad arguments before any launch."""
+    import bench
+    text = re.sub(r"/\*.*?\*/", "", (ROOT / "include" / "q4_mfma_ceiling.h").read_text(), flags=re.S)
+    assert re.findall(r"\b(q4_[a-z0-9_]+)\s*\(", text) == ["q4_mfma_ceiling"]
+    L = bench.floor_lib()
+    assert L.q4_mfma_ceiling(1, 8, None, 1, None) == 1
+    assert L.q4_mfma_ceiling(1, 8, A, 0, None) == 1
+    assert L.q4_mfma_ceiling(1, 0, A, 1, None) == 1
+    assert bench.ceiling_flop(256, 4096) == 256 * 8 * 4096 * 8 * 2 * 32 * 32 * 16
+
+
 def test_trace_build_is_separate(q4lib):
     """libq4trace.so (the measurement build) exports the phase-trace setter;
     libq4.so, the product, does not."""
