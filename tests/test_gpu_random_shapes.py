@@ -4,10 +4,12 @@ against the oracle.  Shapes mix random sizes with sizes a few rows either side
 of the launch plans' boundaries (multiples of 16 rows per compute unit and of
 136 x 16, GEMM row counts near multiples of its 128- and 256-row tiles), K
 from 32 up to 17408 on every path's K granularity (512, 256, 64, 32), and
-fp16 / bf16 / fp32 activations with fp16 or fp32 outputs.  The case list is drawn once from a
-fixed seed, so every run checks the same cases."""
+fp16 / bf16 / fp32 activations with fp16 or fp32 outputs.  The case list is
+drawn once from a fixed seed, so every run checks the same cases.  A longer
+sweep: Q4_RANDOM_CASES=<count> (and Q4_RANDOM_SEED=<seed> for another list)."""
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -18,7 +20,7 @@ from _gpu import to_dev, to_dev_bf16, to_host
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = int(os.environ.get("Q4_RANDOM_CASES", "48"))
 MAX_WEIGHTS = 16_000_000   # n * k, so the host side stays well under a minute in all
 MAX_GEMM_XK = 8_000_000    # m * k for the GEMM's activations
 
@@ -53,7 +55,7 @@ def draw_cases(seed=20261202):
     return cases
 
 
-CASES = draw_cases()
+CASES = draw_cases(int(os.environ.get("Q4_RANDOM_SEED", "20261202")))
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-m{c[1]}-n{c[2]}-k{c[3]}-{c[4]}-{c[5]}"
