@@ -58,6 +58,13 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
   const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lptr_t)(lds)));
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
 }
+// As dma16 with the non-temporal hint (nt): for bytes read once per launch,
+// the packed weights of the decode GEMV, which are then not kept in the
+// caches in place of data that is read again (the activations).
+__device__ __forceinline__ void dma16_nt(const void* src, void* lds) {
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lptr_t)(lds)));
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(base) : "memory");
+}
 
 // Wait until at most N vector-memory operations of this wave are in flight.
 // Emitted through the s_waitcnt builtin (not inline asm) so that the
@@ -150,6 +157,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // address lds + 16 * l (lds uniform, held in M0).  Untracked like dma16.
 __device__ __forceinline__ void dma16_sbase(uint32_t voff, const void* sbase, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+// As dma16_sbase with the non-temporal hint (see dma16_nt).
+__device__ __forceinline__ void dma16_sbase_nt(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lptr_t)(p)));

@@ -215,7 +215,14 @@ __global__ __launch_bounds__((NW + NP) * kWave, 1) void gemv_tile_kernel(
     if constexpr (c < G::niw) {
       const int i0 = (c * CW + cwave) * kWave;
       const uint8_t* ws = wbase + static_cast<int64_t>(p) * (PB * kBlockBytes);
-      if (i0 < wpos && i0 + lane < wpos) dma16_sbase(wsrc[c], ws, sb + i0 * 16);
+      // Weights of at most two row tiles go non-temporal (each byte is read
+      // once: 5120 x 17408 m = 10 16.3 -> 15.9 us, 7168 x 5120 8.0 -> 7.7 us);
+      // with nine tiles the hint measured slower (34816 x 5120 m = 10:
+      // 23.3 -> 24.4 us).
+      if (i0 < wpos && i0 + lane < wpos) {
+        if constexpr (T <= 2) dma16_sbase_nt(wsrc[c], ws, sb + i0 * 16);
+        else dma16_sbase(wsrc[c], ws, sb + i0 * 16);
+      }
     } else {
       constexpr int q = c - G::niw;
       const int i0 = (q * CW + cwave) * kWave;
